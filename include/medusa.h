@@ -1,0 +1,225 @@
+/*
+ * medusa.h -- C ABI of the Medusa verify tree-step library for MI355X (gfx950).
+ *
+ * One verify tree-step of Medusa decoding, as the method is described in the
+ * ICML 2024 paper summary "Medusa: Simple LLM Inference Acceleration Framework
+ * with Multiple Decoding Heads" (section "基准/方法设计", the three components)
+ * and the tutorial page "Medusa 多解码头推理加速全解析" (sections "推理算法"
+ * and "超参数调优指南"):
+ *
+ *   (1) medusa_heads        K Medusa heads on the last hidden state
+ *   (2) medusa_topk         per-head top-k over the vocabulary
+ *       medusa_build_tree   candidate tree from a fixed list of rank paths
+ *       medusa_tree_mask    its node arrays and ancestor bitmask
+ *       medusa_tree_tokens  the token of every tree node
+ *   (3) tree_attention      every node over the prefix KV cache + its ancestors
+ *   (4) typical_accept      typical acceptance and the longest accepted prefix
+ *
+ * Conventions (all calls):
+ *  - Device buffers are plain device pointers owned by the caller; tensors are
+ *    dense, row-major, in the layout given per argument.  Outputs must not
+ *    alias inputs.  Token ids are int32.
+ *  - bf16 tensors hold IEEE bfloat16 bit patterns (uint16); f32 tensors hold
+ *    float.  Device pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Device calls only
+ *    enqueue work; they never synchronise and never allocate device memory.
+ *    Scratch memory is passed in as `ws`/`ws_bytes`, sized by the matching
+ *    *_workspace call.
+ *  - Every argument is checked before anything is launched.  On a non-OK
+ *    status nothing has been enqueued and outputs are untouched;
+ *    medusa_last_error() returns a thread-local description.  A failed launch
+ *    returns MEDUSA_ERR_HIP.  Faults inside kernels surface at the caller's
+ *    next synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MEDUSA_ABI_VERSION 1
+
+typedef enum {
+  MEDUSA_OK = 0,
+  MEDUSA_ERR_ARG = 1,          /* NULL / misaligned pointer, bad scalar argument   */
+  MEDUSA_ERR_SHAPE = 2,        /* sizes that disagree with each other or the tree   */
+  MEDUSA_ERR_TREE = 3,         /* path list that is not a valid candidate tree      */
+  MEDUSA_ERR_UNSUPPORTED = 4,  /* valid request outside the supported limits        */
+  MEDUSA_ERR_WORKSPACE = 5,    /* workspace smaller than the *_workspace size       */
+  MEDUSA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed        */
+  MEDUSA_ERR_STATE = 7         /* tree not uploaded to the device                   */
+} medusa_status;
+
+typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;
+
+typedef void *medusa_stream_t;            /* a hipStream_t */
+typedef struct medusa_tree medusa_tree;   /* opaque candidate tree */
+
+/* Limits checked by the calls below. */
+#define MEDUSA_MAX_TOPK 64        /* k of medusa_topk                         */
+#define MEDUSA_MAX_TREE 1024      /* tree tokens T, root included             */
+#define MEDUSA_MAX_HEADS_M 32     /* rows per medusa_heads launch group       */
+
+const char *medusa_last_error(void);      /* thread-local text of the last non-OK status */
+int medusa_abi_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* (1) Medusa heads.  Paper summary, section "基准/方法设计", first component:
+ *     head k (0-based; it predicts the token k+2 places ahead of the last
+ *     accepted one) is the one-layer ResBlock r = h + SiLU(W1_k h) followed
+ *     by the vocabulary projection W2_k r; W1 = 0 reproduces the backbone's
+ *     LM head exactly.  SiLU(x) = x * sigmoid(x).  No biases.
+ *
+ *  dt = MEDUSA_BF16: h, W1, W2, r are bf16; products accumulate in fp32 on
+ *                    the matrix cores; r is rounded to bf16 (nearest-even).
+ *  dt = MEDUSA_F32 : everything fp32.
+ *  h      [M][H]       device, dt       last hidden state, one row per sequence
+ *  W1     [K][H][H]    device, dt       row = output feature
+ *  W2     [K][V][H]    device, dt       row = vocabulary entry
+ *  r      [K][M][H]    device, dt       output of medusa_head_resblock
+ *  logits [K][M][V]    device, float    output
+ *  Limits: H % 128 == 0 for bf16 (H % 4 == 0 for f32); 1 <= M; rows are
+ *  processed in groups of MEDUSA_MAX_HEADS_M (each group streams the weights
+ *  once).  Errors: ERR_ARG (NULL, misaligned), ERR_UNSUPPORTED (H), ERR_HIP.
+ */
+medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dtype dt, int K, int M, int H,
+                                   const void *h, const void *W1, void *r);
+medusa_status medusa_head_vocab(medusa_stream_t stream, medusa_dtype dt, int K, int M, int H,
+                                int V, const void *r, const void *W2, float *logits);
+/* both of the above, in order, on one stream */
+medusa_status medusa_heads(medusa_stream_t stream, medusa_dtype dt, int K, int M, int H, int V,
+                           const void *h, const void *W1, const void *W2, void *r,
+                           float *logits);
+
+/* ------------------------------------------------------------------------- */
+/* (2) Top-k of every row.  Tutorial page, sections "候选生成" and "每头 Top-K":
+ *     each head contributes its top-k tokens.  Order: value descending, then
+ *     token id ascending (-0.0 == +0.0); -inf allowed; NaN is not.
+ *  logits [R][V] device float;  idx [R][k] device int32 (output);
+ *  val    [R][k] device float (output, may be NULL): logits[r][idx].
+ *  Limits: 1 <= k <= min(V, MEDUSA_MAX_TOPK).  ws: medusa_topk_workspace bytes.
+ */
+size_t medusa_topk_workspace(int R, int V, int k);
+medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k, const float *logits,
+                          int32_t *idx, float *val, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------- */
+/* Candidate trees (host calls).  Tutorial page, section "树结构：medusa_choices":
+ * a tree is a list of rank paths; element d of a path is a rank within Medusa
+ * head d's top-k.  Every proper prefix of a path must be in the list.
+ *
+ * Paths are passed flattened: ranks[p * K + d] for d < path_len[p] (entries
+ * beyond path_len[p] are ignored).
+ */
+
+/* Dense tree (tutorial page, "候选生成": Cartesian product of the per-head
+ * top-k): all sum_{d=1..K} k^d paths, depth then lexicographic order.
+ * cap = capacity of path_len (ranks holds cap*K).  *n_paths receives the count. */
+medusa_status medusa_dense_paths(int K, int k, int cap, int32_t *ranks, int32_t *path_len,
+                                 int *n_paths);
+
+/* Greedy sparse tree (paper summary, "方法细节": from per-head top-i accuracies,
+ * repeatedly add the node with the largest expected gain in accept length).
+ * acc[d * rank_cap + i] = accuracy of rank i of head d (host, K*rank_cap).
+ * A node's gain is the product of acc along its path; equal gains (relative
+ * difference below 1e-12) go to the shorter, then lexicographically smaller
+ * path.  Writes n_paths paths in the order they were added. */
+medusa_status medusa_greedy_paths(const double *acc, int K, int rank_cap, int n_paths,
+                                  int32_t *ranks, int32_t *path_len);
+
+/* Validate a path list and build the tree (host memory only).
+ * Node 0 is the root (the greedy next token); node j >= 1 is the j-th path in
+ * (length, lexicographic) order, so parents precede children.
+ * ERR_TREE: length outside [1, K], rank outside [0, k), duplicate, or missing
+ * prefix.  ERR_UNSUPPORTED: T = n_paths + 1 > MEDUSA_MAX_TREE or k > MEDUSA_MAX_TOPK.
+ * The returned tree is owned by the caller (medusa_tree_free). */
+medusa_status medusa_build_tree(const int32_t *ranks, const int32_t *path_len, int n_paths,
+                                int K, int k, medusa_tree **out);
+
+/* Node arrays of a tree (host outputs; every pointer may be NULL).
+ *  T = tokens incl. root, W = ceil(T/64) mask words per row, depth_max, n_leaves;
+ *  mask[T][W]: bit (i % 64) of word i/64 of row j set iff node i is j or one of
+ *             j's ancestors (root included) -- paper summary, FAQ on tree
+ *             attention: a token sees only the predecessors on its own branch;
+ *  parent[T] (-1 for the root), depth[T], rank[T] (-1 for the root);
+ *  retrieve[n_leaves][depth_max+1]: node ids root..leaf per leaf, -1 padded. */
+medusa_status medusa_tree_mask(const medusa_tree *t, int *T, int *W, int *depth_max,
+                               int *n_leaves, uint64_t *mask, int32_t *parent, int32_t *depth,
+                               int32_t *rank, int32_t *retrieve);
+
+/* Position of each tree token: L + depth (paper summary FAQ: positions follow
+ * the tree structure).  pos: host [T]. */
+medusa_status medusa_tree_positions(const medusa_tree *t, int L, int32_t *pos);
+
+/* Copy the tree's arrays to the current HIP device (one allocation, synchronous).
+ * Required once before the device calls that take the tree.  ERR_HIP on failure. */
+medusa_status medusa_tree_upload(medusa_tree *t);
+
+/* Free the host arrays and the device copy.  NULL is ignored. */
+void medusa_tree_free(medusa_tree *t);
+
+/* Token of every node: tree_tok[b][0] = root_tok[b],
+ * tree_tok[b][j] = topk_idx[depth(j)-1][b][rank(j)]  (tutorial page, "候选生成":
+ * a candidate is the base token followed by one choice per head).
+ *  root_tok [B] device int32; topk_idx [K][B][k] device int32 (K >= depth_max,
+ *  k > every rank in the tree); tree_tok [B][T] device int32 (output). */
+medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B, int K,
+                                 int k, const int32_t *root_tok, const int32_t *topk_idx,
+                                 int32_t *tree_tok);
+
+/* ------------------------------------------------------------------------- */
+/* (3) Tree attention.  Paper summary, "基准/方法设计" (second component) and the
+ *     FAQ on tree attention: all candidates share the prefix; node j attends
+ *     to the L prefix positions and to the tree tokens on its own branch
+ *     (its ancestors, the root and itself):
+ *       out[b][j][h] = softmax(scale * q.[Kc ; Kt[anc(j)]]) . [Vc ; Vt[anc(j)]]
+ *  dt = MEDUSA_BF16: bf16 in/out, scores/softmax/accumulation in fp32, the
+ *                    probabilities enter the PV product as bf16;
+ *  dt = MEDUSA_F32 : fp32 throughout.
+ *  q, k_tree, v_tree  [B][T][nh][dh]  device, dt  (tree tokens, already position-encoded)
+ *  k_cache, v_cache   [B][nh][L][dh]  device, dt  (the prefix cache; L may be 0)
+ *  out                [B][T][nh][dh]  device, dt  (output)
+ *  scale: 0 means 1/sqrt(dh).  Limits: dh in {64, 128}.
+ *  ws: tree_attention_workspace bytes (split-prefix partial results). */
+size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t, int B, int nh, int dh,
+                                int L);
+medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                             int B, int nh, int dh, int L, float scale, const void *q,
+                             const void *k_tree, const void *v_tree, const void *k_cache,
+                             const void *v_cache, void *out, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------- */
+/* (4) Typical acceptance.  Paper summary, "基准/方法设计" (third component) and
+ *     "方法细节" (temperature): candidate token x at node c is kept if
+ *       p(x) > min(eps, delta * exp(-H(p))),
+ *     p = softmax(logits[b][parent(c)] / temperature), H its entropy (nats);
+ *     the root is accepted greedily and unconditionally; a node counts only
+ *     if its parent does; the longest accepted prefix wins, equal lengths
+ *     going to the smallest node index.  temperature = 0 is greedy
+ *     verification (p one-hot at the argmax).  eps = posterior_threshold,
+ *     delta = posterior_alpha (tutorial page, "生成调用").
+ *  logits   [B][T][V] device float  verification logits at every tree node
+ *  tree_tok [B][T]    device int32
+ *  accept_len [B]             device int32  accepted candidates after the root
+ *  best_node  [B]             device int32  node that ends the accepted prefix
+ *  next_tok   [B]             device int32  argmax (lowest id) of best's row
+ *  accepted_tok [B][depth_max+1] device int32  tokens root..best, -1 padded
+ *  cand_p, row_thr [B][T]     device float, optional (NULL): p of each node's
+ *                             token under its parent, and each row's threshold
+ *                             (nan where not evaluated).
+ *  Limits: eps, delta >= 0; temperature >= 0.  ws: typical_accept_workspace. */
+size_t typical_accept_workspace(const medusa_tree *t, int B, int V);
+medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
+                             const float *logits, const int32_t *tree_tok, float eps,
+                             float delta, float temperature, int32_t *accept_len,
+                             int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
+                             float *cand_p, float *row_thr, void *ws, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEDUSA_H */

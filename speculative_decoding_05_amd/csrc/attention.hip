@@ -1,0 +1,479 @@
+// Tree attention: every tree node attends to the prefix KV cache and to the
+// tree tokens on its own branch.
+//
+// bf16 path (one block = one sequence b, one head h, 64 tree queries, one
+// slice of the prefix).  The block streams its keys in tiles of 64: each tile
+// of K and V is read from HBM once with 16-byte coalesced loads (the next
+// tile is prefetched into registers while the current one is consumed) and
+// staged in LDS, where all 4 waves (16 queries each) use it.  Scores are
+// computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 so that every
+// lane ends up owning one query and 16 keys of the tile: the online-softmax
+// row statistics need only two cross-lane steps, and the probabilities are
+// already in the B-operand layout of the O^T = V^T P^T product (the shared
+// reduction index is the same permutation of the 32 keys on both operands).
+// The tree keys come last, as extra tiles of the last slice, where the
+// ancestor bitmask of each query is applied in registers.  With more than one
+// slice per (b, h) the blocks write unnormalised partials (O, m, l) and a
+// second kernel merges them with log-sum-exp weights.
+#include <math.h>
+
+#include "common.h"
+
+using namespace medusa;
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQB = 64;        // queries per block
+constexpr int kKT = 64;        // keys per tile
+constexpr int kPad = 8;        // bf16 elements of row padding in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMinKeysPerSplit = 64;
+constexpr int kTargetBlocks = 1024;
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+struct Split {
+  int nsplit, per_split;  // keys of the prefix per slice (multiple of kKT)
+};
+
+inline Split choose_split(int B, int nh, int T, int L) {
+  const long pairs = (long)B * nh * ((T + kQB - 1) / kQB);
+  int ns = (int)((kTargetBlocks + pairs - 1) / pairs);
+  const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  int per = (L + ns - 1) / ns;
+  per = (per + kKT - 1) / kKT * kKT;
+  if (per == 0) per = kKT;
+  ns = L > 0 ? (L + per - 1) / per : 1;
+  return {ns, per};
+}
+
+template <int DH>
+struct TileRegs {
+  static constexpr int kChunksPerRow = DH / 8;                     // 16-byte chunks
+  static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
+  static constexpr int kPasses = kKT / kRowsPerPass;
+  u32x4_t k[kPasses], v[kPasses];
+};
+
+// Load one tile of 64 keys (rows [r0, r0+64) of a segment) into registers;
+// rows >= rend are zero.  Row i of the segment lives at base + i * row_stride.
+template <int DH>
+__device__ __forceinline__ void load_tile(TileRegs<DH> &t, const uint16_t *kbase,
+                                          const uint16_t *vbase, long row_stride, int r0, int rend) {
+  using TR = TileRegs<DH>;
+  const int c = threadIdx.x % TR::kChunksPerRow;
+#pragma unroll
+  for (int p = 0; p < TR::kPasses; ++p) {
+    const int row = r0 + p * TR::kRowsPerPass + threadIdx.x / TR::kChunksPerRow;
+    if (row < rend) {
+      const size_t off = (size_t)row * row_stride + c * 8;
+      t.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kbase + off));
+      t.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vbase + off));
+    } else {
+      t.k[p] = u32x4_t{0u, 0u, 0u, 0u};
+      t.v[p] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)[DH + kPad],
+                                           uint16_t (*vs)[DH + kPad]) {
+  using TR = TileRegs<DH>;
+  const int c = threadIdx.x % TR::kChunksPerRow;
+#pragma unroll
+  for (int p = 0; p < TR::kPasses; ++p) {
+    const int row = p * TR::kRowsPerPass + threadIdx.x / TR::kChunksPerRow;
+    *reinterpret_cast<u32x4_t *>(&ks[row][c * 8]) = t.k[p];
+    *reinterpret_cast<u32x4_t *>(&vs[row][c * 8]) = t.v[p];
+  }
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) void tree_attn_bf16(
+    int B, int nh, int T, int W, int L, float scale_log2, int qgroups, int nsplit, int per_split,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
+    const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const uint64_t *__restrict__ mask,
+    uint16_t *__restrict__ out, float *__restrict__ ws_o, float2 *__restrict__ ws_ml) {
+  constexpr int DS = DH / 32;  // 32-wide reduction steps over the head dim
+  constexpr int DT = DH / 16;  // 16-wide output tiles over the head dim
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kKT][DH + kPad];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kKT][DH + kPad];
+
+  const int nblocks = gridDim.x;
+  int lb = xcd_remap(blockIdx.x, nblocks);
+  const int split = lb % nsplit;
+  lb /= nsplit;
+  const int qg = lb % qgroups;
+  lb /= qgroups;
+  const int h = lb % nh;
+  const int b = lb / nh;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tq = qg * kQB + wave * 16 + lr;  // this lane's query (tree node)
+  const bool qvalid = tq < T;
+
+  // Q^T as the B operand: lane holds q[tq][32s + 8lg .. +8]
+  u32x4_t qreg[DS];
+  {
+    const uint16_t *qp = q + (((size_t)b * T + (qvalid ? tq : 0)) * nh + h) * DH + lg * 8;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qreg[s] = qvalid ? *reinterpret_cast<const u32x4_t *>(qp + s * 32) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+
+  // key ranges: prefix slice [c0, c1), then (last slice only) the T tree keys
+  const int c0 = split * per_split;
+  const int c1 = min(L, c0 + per_split);
+  const int ncache = c1 > c0 ? (c1 - c0 + kKT - 1) / kKT : 0;
+  const bool last = split == nsplit - 1;
+  const int ntree = last ? (T + kKT - 1) / kKT : 0;
+  const int ntiles = ncache + ntree;
+
+  const long cache_stride = DH;
+  const long tree_stride = (long)nh * DH;
+  const uint16_t *kc_bh = kc + ((size_t)b * nh + h) * L * DH;
+  const uint16_t *vc_bh = vc + ((size_t)b * nh + h) * L * DH;
+  const uint16_t *kt_bh = kt + ((size_t)b * T * nh + h) * DH;
+  const uint16_t *vt_bh = vt + ((size_t)b * T * nh + h) * DH;
+
+  f32x4_t oacc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  TileRegs<DH> regs;
+  auto fetch = [&](int tile) {
+    if (tile < ncache)
+      load_tile<DH>(regs, kc_bh, vc_bh, cache_stride, c0 + tile * kKT, c1);
+    else
+      load_tile<DH>(regs, kt_bh, vt_bh, tree_stride, (tile - ncache) * kKT, T);
+  };
+  if (ntiles > 0) fetch(0);
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();  // previous tile fully consumed
+    store_tile<DH>(regs, ks, vs);
+    __syncthreads();
+    if (tile + 1 < ntiles) fetch(tile + 1);
+
+    const bool is_tree = tile >= ncache;
+    int kend;
+    uint64_t mword = ~0ull;
+    if (is_tree) {
+      const int tt = tile - ncache;
+      kend = T - tt * kKT;
+      mword = qvalid ? mask[(size_t)tq * W + tt] : 0ull;
+    } else {
+      kend = c1 - (c0 + tile * kKT);
+    }
+
+    // S^T for 4 sub-tiles of 16 keys: lane holds S[tq][key 16*st + 4*lg + v]
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&ks[st * 16 + lr][s * 32 + lg * 8]);
+        sacc[st] = mfma(a, qreg[s], sacc[st]);
+      }
+    }
+    float x[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = st * 16 + lg * 4 + v;
+        const bool ok = key < kend && ((mword >> key) & 1ull);
+        x[st][v] = ok ? sacc[st][v] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[st][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        x[st][v] = exp2f(x[st][v] - m_use);
+        psum += x[st][v];
+      }
+    l_lane = l_lane * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+
+    // O^T += V^T P^T over two 32-key halves.  Reduction slot 8*lg + e maps to
+    // key 32*hf + 4*lg + e (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4).
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4_t pb;
+      pb[0] = pack2(x[2 * hf][0], x[2 * hf][1]);
+      pb[1] = pack2(x[2 * hf][2], x[2 * hf][3]);
+      pb[2] = pack2(x[2 * hf + 1][0], x[2 * hf + 1][1]);
+      pb[3] = pack2(x[2 * hf + 1][2], x[2 * hf + 1][3]);
+      const int r0 = hf * 32 + lg * 4;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const int col = d * 16 + lr;
+        u32x4_t a;
+        a[0] = (uint32_t)vs[r0 + 0][col] | ((uint32_t)vs[r0 + 1][col] << 16);
+        a[1] = (uint32_t)vs[r0 + 2][col] | ((uint32_t)vs[r0 + 3][col] << 16);
+        a[2] = (uint32_t)vs[r0 + 16][col] | ((uint32_t)vs[r0 + 17][col] << 16);
+        a[3] = (uint32_t)vs[r0 + 18][col] | ((uint32_t)vs[r0 + 19][col] << 16);
+        oacc[d] = mfma(a, pb, oacc[d]);
+      }
+    }
+  }
+
+  float l_tot = l_lane + __shfl_xor(l_lane, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!qvalid) return;
+  // lane holds O[tq][16*d + 4*lg + v]
+  if (nsplit == 1) {
+    const float inv = 1.f / l_tot;
+    uint16_t *op = out + (((size_t)b * T + tq) * nh + h) * DH + lg * 4;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      uint2 w;
+      w.x = pack2(oacc[d][0] * inv, oacc[d][1] * inv);
+      w.y = pack2(oacc[d][2] * inv, oacc[d][3] * inv);
+      *reinterpret_cast<uint2 *>(op + d * 16) = w;
+    }
+  } else {
+    const size_t row = (((size_t)split * B + b) * nh + h) * T + tq;
+    float *op = ws_o + row * DH + lg * 4;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      *reinterpret_cast<float4 *>(op + d * 16) = make_float4(oacc[d][0], oacc[d][1], oacc[d][2], oacc[d][3]);
+    if (lg == 0) ws_ml[row] = make_float2(m_run, l_tot);
+  }
+}
+
+// Merge the slices of one (b, h, node) row: weights 2^(m_s - M).
+template <int DH>
+__global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T, int nsplit,
+                                                            const float *__restrict__ ws_o,
+                                                            const float2 *__restrict__ ws_ml,
+                                                            uint16_t *__restrict__ out) {
+  constexpr int TPR = DH / 4;  // threads per row, 4 values each
+  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 4;
+  const long nrows = (long)B * nh * T;
+  if (row >= nrows) return;
+  const size_t stride = (size_t)nrows;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[s * stride + row].x);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = ws_ml[s * stride + row];
+    const float w = exp2f(ml.x - Mu);
+    l += w * ml.y;
+    const float4 p = *reinterpret_cast<const float4 *>(ws_o + (s * stride + row) * DH + c);
+    o.x += w * p.x;
+    o.y += w * p.y;
+    o.z += w * p.z;
+    o.w += w * p.w;
+  }
+  const float inv = 1.f / l;
+  // row = (b*nh + h)*T + t  ->  out[b][t][h][:]
+  const int t = row % T;
+  const int bh = row / T;
+  const int h = bh % nh, b = bh / nh;
+  uint2 w;
+  w.x = pack2(o.x * inv, o.y * inv);
+  w.y = pack2(o.z * inv, o.w * inv);
+  *reinterpret_cast<uint2 *>(out + (((size_t)b * T + t) * nh + h) * DH + c) = w;
+}
+
+// fp32 path: block = (b, h, 32 queries); keys = lanes; K/V tiles in LDS.
+constexpr int kF32Q = 32;
+template <int DH>
+__global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W, int L, float scale,
+                                                     int qgroups, const float *__restrict__ q,
+                                                     const float *__restrict__ kt,
+                                                     const float *__restrict__ vt,
+                                                     const float *__restrict__ kc,
+                                                     const float *__restrict__ vc,
+                                                     const uint64_t *__restrict__ mask,
+                                                     float *__restrict__ out) {
+  constexpr int DPL = DH / 64;  // output dims per lane
+  __shared__ float ks[kKT][DH + 1];
+  __shared__ float vs[kKT][DH];
+  __shared__ float qs[kF32Q][DH];
+  const int qg = blockIdx.x % qgroups;
+  const int h = (blockIdx.x / qgroups) % nh;
+  const int b = blockIdx.x / (qgroups * nh);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int e = threadIdx.x; e < kF32Q * DH; e += 256) {
+    const int qi = e / DH, d = e % DH, t = qg * kF32Q + qi;
+    qs[qi][d] = t < T ? q[(((size_t)b * T + t) * nh + h) * DH + d] : 0.f;
+  }
+  float m[8], l[8], o[8][DPL];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    m[u] = -INFINITY;
+    l[u] = 0.f;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[u][j] = 0.f;
+  }
+  const int ncache = (L + kKT - 1) / kKT;
+  const int ntiles = ncache + (T + kKT - 1) / kKT;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const bool is_tree = tile >= ncache;
+    const int r0 = is_tree ? (tile - ncache) * kKT : tile * kKT;
+    const int rend = is_tree ? T : L;
+    __syncthreads();
+    for (int e = threadIdx.x; e < kKT * DH; e += 256) {
+      const int r = e / DH, d = e % DH, row = r0 + r;
+      float kv = 0.f, vv = 0.f;
+      if (row < rend) {
+        const size_t off = is_tree ? (((size_t)b * T + row) * nh + h) * DH + d
+                                   : (((size_t)b * nh + h) * L + row) * DH + d;
+        kv = is_tree ? kt[off] : kc[off];
+        vv = is_tree ? vt[off] : vc[off];
+      }
+      ks[r][d] = kv;
+      vs[r][d] = vv;
+    }
+    __syncthreads();
+    const int key = r0 + lane;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qi = wave * 8 + u, t = qg * kF32Q + qi;
+      float s = 0.f;
+#pragma unroll 8
+      for (int d = 0; d < DH; ++d) s += qs[qi][d] * ks[lane][d];
+      bool ok = key < rend;
+      if (is_tree) ok = ok && t < T && ((mask[(size_t)t * W + (tile - ncache)] >> lane) & 1ull);
+      float x = ok ? s * scale : -INFINITY;
+      float mx = x;
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m[u], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = expf(m[u] - m_use);
+      const float p = expf(x - m_use);
+      float ps = p;
+      for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+      l[u] = l[u] * alpha + ps;
+      m[u] = m_new;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[u][j] *= alpha;
+#pragma unroll 4
+      for (int jk = 0; jk < kKT; ++jk) {
+        const float pj = __shfl(p, jk);
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) o[u][j] += pj * vs[jk][lane + 64 * j];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int t = qg * kF32Q + wave * 8 + u;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out[(((size_t)b * T + t) * nh + h) * DH + lane + 64 * j] = o[u][j] / l[u];
+  }
+}
+
+template <int DH>
+medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, int L, float scale,
+                          const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                          const void *v_cache, void *out, void *ws) {
+  const Split sp = choose_split(B, nh, t->T, L);
+  const int qgroups = (t->T + kQB - 1) / kQB;
+  const long nblocks = (long)B * nh * qgroups * sp.nsplit;
+  if (nblocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: grid too large");
+  float *ws_o = nullptr;
+  float2 *ws_ml = nullptr;
+  if (sp.nsplit > 1) {
+    ws_o = static_cast<float *>(ws);
+    ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
+  }
+  hipLaunchKernelGGL((tree_attn_bf16<DH>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
+                     t->W, L, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
+                     static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
+                     static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
+                     static_cast<const uint16_t *>(v_cache), t->d_mask, static_cast<uint16_t *>(out),
+                     ws_o, ws_ml);
+  medusa_status s = check_launch("tree_attention");
+  if (s != MEDUSA_OK || sp.nsplit == 1) return s;
+  const long rows = (long)B * nh * t->T;
+  const int rpb = 256 / (DH / 4);
+  hipLaunchKernelGGL((tree_attn_merge_bf16<DH>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+                     B, nh, t->T, sp.nsplit, ws_o, ws_ml, static_cast<uint16_t *>(out));
+  return check_launch("tree_attention merge");
+}
+
+template <int DH>
+medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, int L, float scale,
+                         const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                         const void *v_cache, void *out) {
+  const int qgroups = (t->T + kF32Q - 1) / kF32Q;
+  hipLaunchKernelGGL((tree_attn_f32<DH>), dim3(B * nh * qgroups), dim3(256), 0, st, B, nh, t->T, t->W, L,
+                     scale, qgroups, static_cast<const float *>(q), static_cast<const float *>(k_tree),
+                     static_cast<const float *>(v_tree), static_cast<const float *>(k_cache),
+                     static_cast<const float *>(v_cache), t->d_mask, static_cast<float *>(out));
+  return check_launch("tree_attention");
+}
+
+}  // namespace
+
+extern "C" size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t, int B, int nh,
+                                           int dh, int L) {
+  if (!t || B < 1 || nh < 1 || dh < 1 || L < 0 || dt != MEDUSA_BF16) return 0;
+  const Split sp = choose_split(B, nh, t->T, L);
+  if (sp.nsplit == 1) return 0;
+  return (size_t)sp.nsplit * B * nh * t->T * (dh + 2) * sizeof(float);
+}
+
+extern "C" medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                                        int B, int nh, int dh, int L, float scale, const void *q,
+                                        const void *k_tree, const void *v_tree, const void *k_cache,
+                                        const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+  medusa_status s = check_tree_on_device(t);
+  if (s != MEDUSA_OK) return s;
+  if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return fail(MEDUSA_ERR_ARG, "tree_attention: unknown dtype");
+  if (B < 1 || nh < 1 || L < 0) return fail(MEDUSA_ERR_ARG, "tree_attention: B=%d nh=%d L=%d", B, nh, L);
+  if (dh != 64 && dh != 128) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: dh=%d not in {64, 128}", dh);
+  if (!(scale >= 0.f) || !isfinite(scale)) return fail(MEDUSA_ERR_ARG, "tree_attention: bad scale");
+  if (!q || !k_tree || !v_tree || !out || (L > 0 && (!k_cache || !v_cache)))
+    return fail(MEDUSA_ERR_ARG, "tree_attention: NULL pointer");
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
+      (L > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
+    return fail(MEDUSA_ERR_ARG, "tree_attention: pointers must be 16-byte aligned");
+  const size_t need = tree_attention_workspace(dt, t, B, nh, dh, L);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(MEDUSA_ERR_WORKSPACE, "tree_attention: workspace %zu < %zu", ws_bytes, need);
+  if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "tree_attention: workspace must be 16-byte aligned");
+  const float sc = scale == 0.f ? 1.0f / sqrtf((float)dh) : scale;
+  hipStream_t st = as_stream(stream);
+  if (dt == MEDUSA_BF16)
+    return dh == 128 ? launch_bf16<128>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+                     : launch_bf16<64>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+  return dh == 128 ? launch_f32<128>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out)
+                   : launch_f32<64>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out);
+}

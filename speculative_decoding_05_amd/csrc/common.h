@@ -1,0 +1,56 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "medusa.h"
+
+// Candidate tree: host arrays plus one device copy (see medusa_tree_upload).
+struct medusa_tree {
+  int K = 0, k = 0, T = 0, W = 0, depth_max = 0, n_leaves = 0, n_internal = 0;
+  std::vector<int32_t> parent, depth, rank, retrieve;
+  std::vector<int32_t> internal;  // nodes with children, ascending
+  std::vector<int32_t> slot;      // node -> index in `internal`, -1 for leaves
+  std::vector<uint64_t> mask;     // [T][W]
+  // device copy (valid after upload)
+  void *d_base = nullptr;
+  int device = -1;
+  const uint64_t *d_mask = nullptr;
+  const int32_t *d_parent = nullptr, *d_depth = nullptr, *d_rank = nullptr;
+  const int32_t *d_internal = nullptr, *d_slot = nullptr;
+};
+
+namespace medusa {
+
+medusa_status fail(medusa_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+medusa_status check_launch(const char *what);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(medusa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+medusa_status check_tree_on_device(const medusa_tree *t);
+
+// bf16 helpers (bit patterns held in uint16)
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
+}
+__host__ __device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // nan
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Launch-wide XCD-aware block index: the hardware deals consecutive block ids
+// round-robin over the 8 XCDs; remapping makes consecutive *logical* ids land
+// on one XCD so that blocks sharing data share that XCD's L2.
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  const int n8 = nblocks / 8;
+  if (bid >= n8 * 8) return bid;
+  return (bid % 8) * n8 + bid / 8;
+}
+
+}  // namespace medusa

@@ -1,0 +1,164 @@
+// Per-row top-k over the vocabulary, and the tree-token gather.
+//
+// Each element becomes a distinct 64-bit key: the order-preserving image of
+// the float (with -0.0 folded onto +0.0) in the high word and the bitwise
+// complement of the index in the low word, so that "larger key" means
+// "larger value, then smaller index" and every row has one exact answer.
+// Stage 1: a block of 256 threads holds a 2048-element chunk of a row in
+// registers and extracts its k largest keys by k rounds of block-wide max
+// (wave butterfly, then 4 wave results through LDS).  Stage 2: one block per
+// row merges the chunks' candidates the same way.
+#include "common.h"
+
+using namespace medusa;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = 8;
+constexpr int kChunk = kThreads * kPerThread;  // 2048
+constexpr int kMergeMax = kChunk;              // candidates stage 2 can hold
+
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
+  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(mono) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int off) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), off);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), off);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// k rounds: each round finds the block-wide largest remaining key, removes it
+// from its (unique) owner and appends it to out[] (written by thread 0).
+template <int E>
+__device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_t (*s_wave)[4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int round = 0; round < k; ++round) {
+    uint64_t best = 0;
+    int bi = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (keys[e] > best) {
+        best = keys[e];
+        bi = e;
+      }
+    uint64_t w = best;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint64_t o = shfl_xor_u64(w, off);
+      w = o > w ? o : w;
+    }
+    uint64_t *buf = s_wave[round & 1];  // alternate buffers: one barrier per round
+    if (lane == 0) buf[wave] = w;
+    __syncthreads();
+    uint64_t g = buf[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) g = buf[i] > g ? buf[i] : g;
+    if (g != 0 && best == g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e == bi) keys[e] = 0;
+    }
+    if (threadIdx.x == 0) out[round] = g;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_stage1(const float *__restrict__ logits, int V,
+                                                        int k, int nchunks, uint64_t *__restrict__ part) {
+  __shared__ uint64_t s_wave[2][4];
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const float *z = logits + (size_t)row * V;
+  uint64_t keys[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = chunk * kChunk + e * kThreads + threadIdx.x;
+    keys[e] = i < V ? make_key(z[i], static_cast<uint32_t>(i)) : 0ull;
+  }
+  block_extract(keys, k, part + ((size_t)row * nchunks + chunk) * k, s_wave);
+}
+
+__global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict__ logits, int V,
+                                                        int k, int nchunks,
+                                                        const uint64_t *__restrict__ part,
+                                                        int32_t *__restrict__ idx,
+                                                        float *__restrict__ val) {
+  __shared__ uint64_t s_wave[2][4];
+  __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
+  const int row = blockIdx.x;
+  const int n = nchunks * k;
+  const uint64_t *p = part + (size_t)row * n;
+  uint64_t keys[kPerThread];
+#pragma unroll
+  for (int e = 0; e < kPerThread; ++e) {
+    const int i = e * kThreads + threadIdx.x;
+    keys[e] = i < n ? p[i] : 0ull;
+  }
+  block_extract(keys, k, s_out, s_wave);
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += kThreads) {
+    const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s_out[j]);
+    idx[(size_t)row * k + j] = static_cast<int32_t>(id);
+    if (val) val[(size_t)row * k + j] = logits[(size_t)row * V + id];
+  }
+}
+
+__global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restrict__ depth,
+                                   const int32_t *__restrict__ rank, const int32_t *__restrict__ root,
+                                   const int32_t *__restrict__ topk_idx, int32_t *__restrict__ tok) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * T) return;
+  const int b = i / T, j = i % T;
+  tok[i] = j == 0 ? root[b] : topk_idx[((size_t)(depth[j] - 1) * B + b) * k + rank[j]];
+}
+
+inline int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
+
+}  // namespace
+
+extern "C" size_t medusa_topk_workspace(int R, int V, int k) {
+  if (R < 1 || V < 1 || k < 1) return 0;
+  return (size_t)R * chunks_for(V) * k * sizeof(uint64_t);
+}
+
+extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k,
+                                     const float *logits, int32_t *idx, float *val, void *ws,
+                                     size_t ws_bytes) {
+  if (R < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "medusa_topk: R=%d V=%d", R, V);
+  if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "medusa_topk: k=%d outside [1, V=%d]", k, V);
+  if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: k=%d > %d", k, MEDUSA_MAX_TOPK);
+  if (!logits || !idx || !ws) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL pointer");
+  const int nchunks = chunks_for(V);
+  if ((long)nchunks * k > kMergeMax)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: V=%d with k=%d exceeds the merge capacity", V, k);
+  if (ws_bytes < medusa_topk_workspace(R, V, k))
+    return fail(MEDUSA_ERR_WORKSPACE, "medusa_topk: workspace %zu < %zu", ws_bytes,
+                medusa_topk_workspace(R, V, k));
+  if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: R=%d > 65535", R);
+  hipStream_t st = as_stream(stream);
+  uint64_t *part = static_cast<uint64_t *>(ws);
+  hipLaunchKernelGGL(topk_stage1, dim3(nchunks, R), dim3(kThreads), 0, st, logits, V, k, nchunks, part);
+  medusa_status s = check_launch("medusa_topk stage 1");
+  if (s != MEDUSA_OK) return s;
+  hipLaunchKernelGGL(topk_stage2, dim3(R), dim3(kThreads), 0, st, logits, V, k, nchunks, part, idx, val);
+  return check_launch("medusa_topk stage 2");
+}
+
+extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B,
+                                            int K, int k, const int32_t *root_tok,
+                                            const int32_t *topk_idx, int32_t *tree_tok) {
+  medusa_status s = check_tree_on_device(t);
+  if (s != MEDUSA_OK) return s;
+  if (B < 1) return fail(MEDUSA_ERR_ARG, "medusa_tree_tokens: B=%d", B);
+  if (!root_tok || !topk_idx || !tree_tok) return fail(MEDUSA_ERR_ARG, "medusa_tree_tokens: NULL pointer");
+  if (K < t->depth_max || k < t->k)
+    return fail(MEDUSA_ERR_SHAPE, "medusa_tree_tokens: top-k block [K=%d][k=%d] smaller than the tree's [%d][%d]",
+                K, k, t->depth_max, t->k);
+  const int n = B * t->T;
+  hipLaunchKernelGGL(tree_tokens_kernel, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), B,
+                     t->T, k, t->d_depth, t->d_rank, root_tok, topk_idx, tree_tok);
+  return check_launch("medusa_tree_tokens");
+}

@@ -1,0 +1,119 @@
+"""One Medusa verify tree-step on the GPU, assembled from the C-ABI calls.
+
+heads -> per-head top-k -> tree tokens -> tree attention -> typical
+acceptance, all enqueued on torch's current stream with preallocated
+buffers and workspaces (nothing is allocated inside `run`).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as mb
+from . import configs, synth
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a synth tensor: uint16 bf16 bit patterns or float32 / int32."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def build_tree(cfg: configs.Config) -> mb.Tree:
+    """The configuration's candidate tree, built by the library."""
+    spec = cfg.tree
+    if spec.kind == "dense":
+        paths = mb.dense_paths(cfg.K, spec.k)
+    else:
+        acc = np.array([[configs.acc_float(d, i) for i in range(spec.rank_cap)] for d in range(cfg.K)])
+        paths = mb.greedy_paths(acc, spec.n_paths)
+    return mb.Tree(paths, cfg.K, spec.k).upload()
+
+
+class Step:
+    """Device buffers of one configuration and the launch sequence of one step.
+
+    `copies` > 1 keeps several copies of every per-step input (hidden state,
+    tree Q/K/V, KV cache, verification logits) so that consecutive steps can
+    rotate through them and not be served from the last-level cache.
+    """
+
+    def __init__(self, cfg: configs.Config, tree: mb.Tree, host: dict, copies: int = 1, device="cuda"):
+        self.cfg, self.tree, self.copies = cfg, tree, copies
+        B, K, V, H, k, T = cfg.B, cfg.K, cfg.V, cfg.H, cfg.k, tree.T
+        dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.dt = dt
+        dev = device
+        self.W1 = to_device(host["W1"], dev)
+        self.W2 = to_device(host["W2"], dev)
+        self.root = to_device(host["root_tok"].astype(np.int32), dev)
+        self.h = [to_device(host["h"], dev) for _ in range(copies)]
+        self.q = [to_device(host["q"], dev) for _ in range(copies)]
+        self.kt = [to_device(host["kt"], dev) for _ in range(copies)]
+        self.vt = [to_device(host["vt"], dev) for _ in range(copies)]
+        self.kc = [to_device(host["kc"], dev) for _ in range(copies)]
+        self.vc = [to_device(host["vc"], dev) for _ in range(copies)]
+        self.vlogits = [None] * copies
+        if host.get("vlogits") is not None:
+            self.set_verify_logits(host["vlogits"])
+        self.r = torch.empty((K, B, H), dtype=dt, device=dev)
+        self.head_logits = torch.empty((K, B, V), dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((K, B, k), dtype=torch.int32, device=dev)
+        self.tree_tok = torch.empty((B, T), dtype=torch.int32, device=dev)
+        self.attn = torch.empty((B, T, cfg.nh, cfg.dh), dtype=dt, device=dev)
+        self.accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+        self.best = torch.empty(B, dtype=torch.int32, device=dev)
+        self.next_tok = torch.empty(B, dtype=torch.int32, device=dev)
+        self.accepted = torch.empty((B, tree.depth_max + 1), dtype=torch.int32, device=dev)
+        dcode = mb.BF16 if cfg.dtype == "bf16" else mb.F32
+        self.ws_topk = mb.workspace(mb.medusa_topk_workspace(K * B, V, k), dev)
+        self.ws_attn = mb.workspace(mb.tree_attention_workspace(dcode, tree, B, cfg.nh, cfg.dh, cfg.L), dev)
+        self.ws_acc = mb.workspace(mb.typical_accept_workspace(tree, B, V), dev)
+
+    def set_verify_logits(self, vl: np.ndarray):
+        for i in range(self.copies):
+            self.vlogits[i] = to_device(vl.astype(np.float32))
+
+    # -- the stages -------------------------------------------------------------
+    def heads(self, i=0):
+        mb.medusa_head_resblock(self.h[i], self.W1, self.r)
+
+    def heads_vocab(self, i=0):
+        mb.medusa_head_vocab(self.r, self.W2, self.head_logits)
+
+    def topk_and_tokens(self, i=0):
+        mb.medusa_topk(self.head_logits, self.cfg.k, self.topk_idx, None, self.ws_topk)
+        mb.medusa_tree_tokens(self.tree, self.root, self.topk_idx, self.tree_tok)
+
+    def attention(self, i=0):
+        mb.tree_attention(self.tree, self.q[i], self.kt[i], self.vt[i], self.kc[i], self.vc[i], self.attn,
+                          0.0, self.ws_attn)
+
+    def accept(self, i=0):
+        c = self.cfg
+        mb.typical_accept(self.tree, self.vlogits[i], self.tree_tok, c.eps, c.delta, c.temperature,
+                          self.accept_len, self.best, self.next_tok, self.accepted, None, None, self.ws_acc)
+
+    def run(self, i=0):
+        """Enqueue one whole verify tree-step on the current stream."""
+        self.heads(i)
+        self.heads_vocab(i)
+        self.topk_and_tokens(i)
+        self.attention(i)
+        self.accept(i)
+
+
+def host_inputs(cfg: configs.Config, T: int, B: int | None = None, L: int | None = None) -> dict:
+    """All seeded inputs of a configuration except the verification logits."""
+    W1, W2 = synth.head_weights(cfg)
+    kc, vc = synth.kv_cache(cfg, B, L)
+    q, kt, vt = synth.tree_qkv(cfg, T, B)
+    return {"W1": W1, "W2": W2, "h": synth.hidden(cfg, B), "root_tok": synth.root_tokens(cfg, B),
+            "q": q, "kt": kt, "vt": vt, "kc": kc, "vc": vc}
+
+
+def verify_logits_for(cfg: configs.Config, tree: mb.Tree, topk_idx: np.ndarray, root_tok: np.ndarray):
+    """Planted verification logits for the given top-k candidates (synthetic)."""
+    return synth.verification_logits(cfg.cfg_id, cfg.V, tree.parent, tree.depth, tree.rank, topk_idx,
+                                     root_tok, configs.acc_float, cfg.k)
