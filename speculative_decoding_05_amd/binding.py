@@ -38,6 +38,11 @@ SIGNATURES = {
     "medusa_head_resblock": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_head_vocab": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_heads": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
+    "medusa_packed_weight_bytes": (_sz, [_i, _i, _i]),
+    "medusa_pack_weights": (_i, [_p, _i, _i, _i, _p, _p]),
+    "medusa_head_resblock_packed": (_i, [_p, _i, _i, _i, _p, _p, _p]),
+    "medusa_head_vocab_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
+    "medusa_heads_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
     "medusa_topk_workspace": (_sz, [_i, _i, _i]),
     "medusa_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_dense_paths": (_i, [_i, _i, _i, _ip, _ip, ctypes.POINTER(_i)]),
@@ -105,9 +110,9 @@ def _dev(*ts):
 
 
 def workspace(nbytes, device=None):
-    """Device scratch buffer of at least nbytes (16-byte aligned)."""
+    """Zero-filled device scratch buffer of at least nbytes (16-byte aligned)."""
     torch = _torch()
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
 
 
 # ---------------------------------------------------------------- heads
@@ -133,6 +138,40 @@ def medusa_heads(h, W1, W2, r, logits):
     M = h.shape[0]
     check(lib.medusa_heads(_stream(), _dtype_code(h), K, M, H, V, _ptr(h), _ptr(W1), _ptr(W2),
                            _ptr(r), _ptr(logits)))
+    return logits
+
+
+class PackedWeights:
+    """bf16 head weights [K][N][H] reordered once into the matrix-core fragment order."""
+
+    def __init__(self, W):
+        torch = _torch()
+        _dev(W)
+        if W.dtype != torch.bfloat16:
+            raise TypeError("packed weights are bf16")
+        self.K, self.N, self.H = W.shape
+        nbytes = lib.medusa_packed_weight_bytes(self.K, self.N, self.H)
+        self.data = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W.device)
+        check(lib.medusa_pack_weights(_stream(), self.K, self.N, self.H, _ptr(W), _ptr(self.data)))
+
+
+def medusa_head_resblock_packed(h, W1p, r):
+    _dev(h, r)
+    check(lib.medusa_head_resblock_packed(_stream(), W1p.K, h.shape[0], W1p.H, _ptr(h), _ptr(W1p.data), _ptr(r)))
+    return r
+
+
+def medusa_head_vocab_packed(r, W2p, logits):
+    _dev(r, logits)
+    check(lib.medusa_head_vocab_packed(_stream(), W2p.K, r.shape[1], W2p.H, W2p.N, _ptr(r), _ptr(W2p.data),
+                                       _ptr(logits)))
+    return logits
+
+
+def medusa_heads_packed(h, W1p, W2p, r, logits):
+    _dev(h, r, logits)
+    check(lib.medusa_heads_packed(_stream(), W2p.K, h.shape[0], W2p.H, W2p.N, _ptr(h), _ptr(W1p.data),
+                                  _ptr(W2p.data), _ptr(r), _ptr(logits)))
     return logits
 
 

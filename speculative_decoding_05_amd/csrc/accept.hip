@@ -1,10 +1,12 @@
 // Typical acceptance over the candidate tree.
 //
-// Row pass (one block per 4096-wide chunk of a verification row of a node
-// that has children): the chunk is held in registers; a block max/argmax
-// (lowest index on ties) is followed by S = sum e^(y-m) and
-// E = sum e^(y-m) (y-m) with y = z / temperature, from which
-// H = ln S - E/S.  Partials (m, S, E, argmax) per chunk go to the workspace.
+// Row pass (one block per 4096-wide chunk of the verification row of a node
+// that has children): every thread folds its 16 values into running
+// statistics of y = z / temperature -- max m, S = sum e^(y-m),
+// E = sum e^(y-m) (y-m) -- and the argmax of z (lowest index on ties); one
+// block reduction merges the statistics (rescaling by e^(m_i - m)) with DPP
+// row steps, readlane and LDS, and the chunk's (m, S, E, argmax) goes to the
+// workspace.  Then H = ln S - E/S.
 // Scan (one block per sequence): merge the chunk partials of every internal
 // row into its threshold min(eps, delta e^-H); decide every candidate against
 // its parent's row; a node is accepted iff every node on its path (the root
@@ -21,14 +23,23 @@ namespace {
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kVec = 4;                         // float4 per thread
-constexpr int kChunk = kThreads * kVec * 4;     // 4096 floats
+constexpr int kThreads = 256;                  // row pass
+constexpr int kVec = 4;                        // float4 per thread
+constexpr int kChunk = kThreads * kVec * 4;    // 4096 floats
+constexpr int kScanThreads = 512;              // scan
+constexpr int kBatch = 8;                      // independent loads issued together
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Part {  // 32 bytes
   float m, S, E, amax_val;
   int amax_idx, pad0, pad1, pad2;
+};
+
+// running statistics: max m of y, S = sum e^(y-m), E = sum e^(y-m)(y-m),
+// argmax (av, ai) of z with the lowest index on ties
+struct Stat {
+  float m, S, E, av;
+  int ai;
 };
 
 __device__ __forceinline__ void arg_better(float &bv, int &bi, float v, int i) {
@@ -38,33 +49,56 @@ __device__ __forceinline__ void arg_better(float &bv, int &bi, float v, int i) {
   }
 }
 
-// block-wide argmax (value desc, index asc); result valid in every thread
-__device__ void block_argmax(float &bv, int &bi, float *s_v, int *s_i) {
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    arg_better(bv, bi, ov, oi);
+__device__ __forceinline__ Stat empty_stat() { return {-INFINITY, 0.f, 0.f, -INFINITY, 0x7fffffff}; }
+
+__device__ __forceinline__ Stat combine(const Stat &a, const Stat &b) {
+  Stat r;
+  r.m = fmaxf(a.m, b.m);
+  r.S = 0.f;
+  r.E = 0.f;
+  if (a.S > 0.f) {
+    const float d = a.m - r.m;
+    const float w = exp2f(d * kLog2e);
+    r.S += w * a.S;
+    r.E += w * (a.E + d * a.S);
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) {
-    s_v[wave] = bv;
-    s_i[wave] = bi;
+  if (b.S > 0.f) {
+    const float d = b.m - r.m;
+    const float w = exp2f(d * kLog2e);
+    r.S += w * b.S;
+    r.E += w * (b.E + d * b.S);
   }
-  __syncthreads();
-  bv = s_v[0];
-  bi = s_i[0];
-  for (int w = 1; w < kThreads / 64; ++w) arg_better(bv, bi, s_v[w], s_i[w]);
+  r.av = a.av;
+  r.ai = a.ai;
+  arg_better(r.av, r.ai, b.av, b.ai);
+  return r;
 }
 
-__device__ float block_sum(float v, float *s) {
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <int CTRL>
+__device__ __forceinline__ Stat dpp_stat(const Stat &s) {
+  return {dppf<CTRL>(s.m), dppf<CTRL>(s.S), dppf<CTRL>(s.E), dppf<CTRL>(s.av),
+          static_cast<int>(dpp<CTRL>(static_cast<uint32_t>(s.ai)))};
+}
+
+__device__ __forceinline__ Stat lane_stat(const Stat &s, int lane) {
+  return {readlanef(s.m, lane), readlanef(s.S, lane), readlanef(s.E, lane), readlanef(s.av, lane),
+          static_cast<int>(readlane(static_cast<uint32_t>(s.ai), lane))};
+}
+
+// block-wide merge; the result is valid in every thread
+template <int NT>
+__device__ Stat block_reduce(Stat s, Stat *sh) {
+  s = combine(s, dpp_stat<kDppXor1>(s));
+  s = combine(s, dpp_stat<kDppXor2>(s));
+  s = combine(s, dpp_stat<kDppHalfMirror>(s));
+  s = combine(s, dpp_stat<kDppMirror>(s));
+  s = combine(combine(lane_stat(s, 0), lane_stat(s, 16)), combine(lane_stat(s, 32), lane_stat(s, 48)));
+  __syncthreads();  // sh may still be read by a previous reduction
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = s;
   __syncthreads();
-  if (lane == 0) s[wave] = v;
-  __syncthreads();
-  float r = 0.f;
-  for (int w = 0; w < kThreads / 64; ++w) r += s[w];
+  Stat r = sh[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = combine(r, sh[w]);
   return r;
 }
 
@@ -73,16 +107,14 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
                                                            const int32_t *__restrict__ internal,
                                                            int nchunks, float inv_tau, int greedy,
                                                            Part *__restrict__ part) {
-  __shared__ float s_v[kThreads / 64];
-  __shared__ int s_i[kThreads / 64];
+  __shared__ Stat sh[kThreads / 64];
   const int chunk = blockIdx.x, slot = blockIdx.y, b = blockIdx.z;
   const int row = internal[slot];
   const float *z = logits + ((size_t)b * T + row) * V;
   const int base = chunk * kChunk;
   const bool vec_ok = (V % 4) == 0;
   float val[kVec][4];
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
+  Stat st = empty_stat();
 #pragma unroll
   for (int u = 0; u < kVec; ++u) {
     const int i0 = base + (u * kThreads + threadIdx.x) * 4;
@@ -96,82 +128,73 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (i0 + j < V) arg_better(bv, bi, val[u][j], i0 + j);
+      if (i0 + j < V) arg_better(st.av, st.ai, val[u][j], i0 + j);
   }
-  block_argmax(bv, bi, s_v, s_i);
-  float S = 0.f, E = 0.f;
-  const float m = bv * inv_tau;  // max of y = z / tau (tau > 0 keeps the order)
-  if (!greedy && m != -INFINITY) {
+  if (!greedy && st.av != -INFINITY) {
+    st.m = st.av * inv_tau;  // max of y (tau > 0 keeps the order)
 #pragma unroll
     for (int u = 0; u < kVec; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float d = val[u][j] * inv_tau - m;  // -inf for padding
+        const float d = val[u][j] * inv_tau - st.m;  // -inf for padding
         const float e = exp2f(d * kLog2e);
-        S += e;
-        E += e == 0.f ? 0.f : e * d;
+        st.S += e;
+        st.E += e == 0.f ? 0.f : e * d;
       }
-    S = block_sum(S, s_v);
-    E = block_sum(E, s_v);
   }
+  st = block_reduce<kThreads>(st, sh);
   if (threadIdx.x == 0) {
     Part p;
-    p.m = m;
-    p.S = S;
-    p.E = E;
-    p.amax_val = bv;
-    p.amax_idx = bi;
+    p.m = st.m;
+    p.S = st.S;
+    p.E = st.E;
+    p.amax_val = st.av;
+    p.amax_idx = st.ai;
     p.pad0 = p.pad1 = p.pad2 = 0;
     part[((size_t)b * n_internal + slot) * nchunks + chunk] = p;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void accept_scan(
+__global__ __launch_bounds__(kScanThreads) void accept_scan(
     const float *__restrict__ logits, const int32_t *__restrict__ tree_tok, int T, int W, int V,
-    int depth_max, int n_internal, int nchunks, const int32_t *__restrict__ internal,
-    const int32_t *__restrict__ slot_of, const int32_t *__restrict__ parent,
-    const int32_t *__restrict__ depth, const uint64_t *__restrict__ mask, float eps, float delta,
-    float inv_tau, int greedy, const Part *__restrict__ part, int32_t *__restrict__ accept_len,
-    int32_t *__restrict__ best_node, int32_t *__restrict__ next_tok,
-    int32_t *__restrict__ accepted_tok, float *__restrict__ cand_p, float *__restrict__ row_thr) {
+    int depth_max, int n_internal, int nchunks, const int32_t *__restrict__ slot_of,
+    const int32_t *__restrict__ parent, const int32_t *__restrict__ depth,
+    const uint64_t *__restrict__ mask, float eps, float delta, float inv_tau, int greedy,
+    const Part *__restrict__ part, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
+    int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ cand_p,
+    float *__restrict__ row_thr) {
   __shared__ float s_m[MEDUSA_MAX_TREE], s_S[MEDUSA_MAX_TREE], s_thr[MEDUSA_MAX_TREE];
   __shared__ int s_amax[MEDUSA_MAX_TREE];
   __shared__ unsigned int s_dec[MEDUSA_MAX_TREE / 32];
-  __shared__ unsigned int s_key[kThreads / 64];
-  __shared__ float s_v[kThreads / 64];
-  __shared__ int s_i[kThreads / 64];
+  __shared__ unsigned int s_key[kScanThreads / 64];
+  __shared__ Stat sh[kScanThreads / 64];
   const int b = blockIdx.x;
-  for (int w = threadIdx.x; w < MEDUSA_MAX_TREE / 32; w += kThreads) s_dec[w] = 0u;
+  const int tid = threadIdx.x;
+  for (int w = tid; w < MEDUSA_MAX_TREE / 32; w += kScanThreads) s_dec[w] = 0u;
 
-  // 1. per internal row: merge chunk partials, threshold
-  for (int sl = threadIdx.x; sl < n_internal; sl += kThreads) {
+  // 1. per internal row: merge the chunk partials, then the threshold
+  for (int sl = tid; sl < n_internal; sl += kScanThreads) {
     const Part *p = part + ((size_t)b * n_internal + sl) * nchunks;
-    float M = -INFINITY, av = -INFINITY;
-    int ai = 0x7fffffff;
-    for (int c = 0; c < nchunks; ++c) {
-      M = fmaxf(M, p[c].m);
-      arg_better(av, ai, p[c].amax_val, p[c].amax_idx);
+    Stat acc = empty_stat();
+    for (int c0 = 0; c0 < nchunks; c0 += kBatch) {
+      Part q[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (c0 + u < nchunks) q[u] = p[c0 + u];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (c0 + u < nchunks) acc = combine(acc, Stat{q[u].m, q[u].S, q[u].E, q[u].amax_val, q[u].amax_idx});
     }
-    float S = 0.f, E = 0.f;
-    if (!greedy) {
-      for (int c = 0; c < nchunks; ++c) {
-        if (p[c].S == 0.f) continue;
-        const float dm = p[c].m - M;
-        const float w = exp2f(dm * kLog2e);
-        S += w * p[c].S;
-        E += w * (p[c].E + dm * p[c].S);
-      }
-    }
-    const float H = greedy ? 0.f : logf(S) - E / S;
-    s_m[sl] = M;
-    s_S[sl] = S;
+    const float H = greedy ? 0.f : logf(acc.S) - acc.E / acc.S;
+    s_m[sl] = acc.m;
+    s_S[sl] = acc.S;
     s_thr[sl] = fminf(eps, delta * expf(-H));
-    s_amax[sl] = ai;
+    s_amax[sl] = acc.ai;
   }
   __syncthreads();
 
   // 2. decisions: candidate c against its parent's row
-  for (int c = threadIdx.x; c < T; c += kThreads) {
+  for (int c = tid; c < T; c += kScanThreads) {
     const int sc = slot_of[c];
     if (row_thr) row_thr[(size_t)b * T + c] = sc >= 0 ? s_thr[sc] : NAN;
     if (c == 0) {
@@ -201,13 +224,12 @@ __global__ __launch_bounds__(kThreads) void accept_scan(
 
   // 3. accepted iff all ancestors but the root decided yes; deepest, then smallest index
   unsigned int key = 0u;
-  for (int c = threadIdx.x; c < T; c += kThreads) {
+  for (int c = tid; c < T; c += kScanThreads) {
     bool acc = true;
     for (int w = 0; w < W; ++w) {
       uint64_t anc = mask[(size_t)c * W + w];
       if (w == 0) anc &= ~1ull;
-      const int i0 = w * 64;
-      const uint64_t dec = (uint64_t)s_dec[i0 >> 5] | ((uint64_t)s_dec[(i0 >> 5) + 1] << 32);
+      const uint64_t dec = (uint64_t)s_dec[2 * w] | ((uint64_t)s_dec[2 * w + 1] << 32);
       if (anc & ~dec) acc = false;
     }
     if (acc) {
@@ -215,18 +237,15 @@ __global__ __launch_bounds__(kThreads) void accept_scan(
       key = k > key ? k : key;
     }
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    const unsigned int o = __shfl_xor(key, off);
-    key = o > key ? o : key;
-  }
-  if ((threadIdx.x & 63) == 0) s_key[threadIdx.x >> 6] = key;
+  key = wave_max_u32(key);
+  if ((tid & 63) == 0) s_key[tid >> 6] = key;
   __syncthreads();
   key = s_key[0];
-  for (int w = 1; w < kThreads / 64; ++w) key = s_key[w] > key ? s_key[w] : key;
+  for (int w = 1; w < kScanThreads / 64; ++w) key = s_key[w] > key ? s_key[w] : key;
   const int alen = (int)(key >> 16);
   const int best = (int)(0xFFFFu - (key & 0xFFFFu));
 
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     accept_len[b] = alen;
     best_node[b] = best;
     int32_t *at = accepted_tok + (size_t)b * (depth_max + 1);
@@ -234,18 +253,37 @@ __global__ __launch_bounds__(kThreads) void accept_scan(
     int d = alen;
     for (int j = best; j != -1; j = parent[j]) at[d--] = tree_tok[(size_t)b * T + j];
   }
-  // 4. next greedy token: argmax of the winner's row
+  // 4. next greedy token: argmax of the winner's row (already known for rows with children)
   const int sb = slot_of[best];
   if (sb >= 0) {
-    if (threadIdx.x == 0) next_tok[b] = s_amax[sb];
-  } else {
-    const float *z = logits + ((size_t)b * T + best) * V;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int i = threadIdx.x; i < V; i += kThreads) arg_better(bv, bi, z[i], i);
-    block_argmax(bv, bi, s_v, s_i);
-    if (threadIdx.x == 0) next_tok[b] = bi;
+    if (tid == 0) next_tok[b] = s_amax[sb];
+    return;
   }
+  const float *z = logits + ((size_t)b * T + best) * V;
+  Stat st = empty_stat();
+  if ((V % 4) == 0) {
+    const int V4 = V / 4;
+    for (int base = tid; base < V4; base += kScanThreads * kBatch) {
+      f32x4_t v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = base + u * kScanThreads;
+        v[u] = i < V4 ? *reinterpret_cast<const f32x4_t *>(z + 4 * i)
+                      : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * (base + u * kScanThreads) + j;
+          if (i < V) arg_better(st.av, st.ai, v[u][j], i);
+        }
+    }
+  } else {
+    for (int i = tid; i < V; i += kScanThreads) arg_better(st.av, st.ai, z[i], i);
+  }
+  st = block_reduce<kScanThreads>(st, sh);
+  if (tid == 0) next_tok[b] = st.ai;
 }
 
 inline int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
@@ -284,9 +322,9 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
     s = check_launch("typical_accept row pass");
     if (s != MEDUSA_OK) return s;
   }
-  hipLaunchKernelGGL(accept_scan, dim3(B), dim3(kThreads), 0, st, logits, tree_tok, t->T, t->W, V,
-                     t->depth_max, t->n_internal, nchunks, t->d_internal, t->d_slot, t->d_parent,
-                     t->d_depth, t->d_mask, eps, delta, inv_tau, greedy, part, accept_len, best_node,
-                     next_tok, accepted_tok, cand_p, row_thr);
+  hipLaunchKernelGGL(accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
+                     t->depth_max, t->n_internal, nchunks, t->d_slot, t->d_parent, t->d_depth, t->d_mask,
+                     eps, delta, inv_tau, greedy, part, accept_len, best_node, next_tok, accepted_tok,
+                     cand_p, row_thr);
   return check_launch("typical_accept scan");
 }

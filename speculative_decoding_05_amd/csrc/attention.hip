@@ -9,12 +9,16 @@
 // computed transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16 so that every
 // lane ends up owning one query and 16 keys of the tile: the online-softmax
 // row statistics need only two cross-lane steps, and the probabilities are
-// already in the B-operand layout of the O^T = V^T P^T product (the shared
-// reduction index is the same permutation of the 32 keys on both operands).
-// The tree keys come last, as extra tiles of the last slice, where the
-// ancestor bitmask of each query is applied in registers.  With more than one
-// slice per (b, h) the blocks write unnormalised partials (O, m, l) and a
-// second kernel merges them with log-sum-exp weights.
+// already in the B-operand layout of the O^T = V^T P^T product.  The V^T
+// A-operand comes straight from the row-major V tile through the LDS
+// transpose read (ds_read_b64_tr_b16): within each 16-lane group lane i
+// receives element (i & 3) of the 8-byte value addressed by lane 4e + (i >> 2),
+// so lanes that address keys k..k+3 at columns d..d+15 in groups of four
+// deliver V[k+e][d+i] to lane i.  The tree keys come last, as extra tiles of
+// the last slice, where the ancestor bitmask of each query is applied in
+// registers; full prefix tiles skip masking.  With more than one slice per
+// (b, h) the blocks write unnormalised partials (O, m, l) and a second kernel
+// merges them with log-sum-exp weights.
 #include <math.h>
 
 #include "common.h"
@@ -26,12 +30,16 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQB = 64;        // queries per block
 constexpr int kKT = 64;        // keys per tile
-constexpr int kPad = 8;        // bf16 elements of row padding in LDS
+constexpr int kPadK = 8;       // row padding (bf16) of the K tile: 16 rows of a b128 read hit distinct banks
+constexpr int kPadV = 16;      // row padding (bf16) of the V tile: 8 rows of a transpose read hit distinct banks
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMinKeysPerSplit = 64;
 constexpr int kTargetBlocks = 1024;
@@ -41,8 +49,16 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) | (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 4 bf16 of V^T from the row-major V tile through the LDS transpose read
+__device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);  // generic -> LDS address space
+  return __builtin_bit_cast(uint2, r);
 }
 
 struct Split {
@@ -92,8 +108,8 @@ __device__ __forceinline__ void load_tile(TileRegs<DH> &t, const uint16_t *kbase
 }
 
 template <int DH>
-__device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)[DH + kPad],
-                                           uint16_t (*vs)[DH + kPad]) {
+__device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)[DH + kPadK],
+                                           uint16_t (*vs)[DH + kPadV]) {
   using TR = TileRegs<DH>;
   const int c = threadIdx.x % TR::kChunksPerRow;
 #pragma unroll
@@ -112,8 +128,8 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float2 *__restrict__ ws_ml) {
   constexpr int DS = DH / 32;  // 32-wide reduction steps over the head dim
   constexpr int DT = DH / 16;  // 16-wide output tiles over the head dim
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kKT][DH + kPad];
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kKT][DH + kPad];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kKT][DH + kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kKT][DH + kPadV];
 
   const int nblocks = gridDim.x;
   int lb = xcd_remap(blockIdx.x, nblocks);
@@ -197,35 +213,51 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
     }
     float x[4][4];
     float mx = -INFINITY;
+    if (is_tree || kend < kKT) {  // partial or tree tile: bounds and ancestor mask
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key = st * 16 + lg * 4 + v;
-        const bool ok = key < kend && ((mword >> key) & 1ull);
-        x[st][v] = ok ? sacc[st][v] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[st][v]);
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int key = st * 16 + lg * 4 + v;
+          const bool ok = key < kend && ((mword >> key) & 1ull);
+          x[st][v] = ok ? sacc[st][v] * scale_log2 : -INFINITY;
+          mx = fmaxf(mx, x[st][v]);
+        }
+    } else {
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[st][v] = sacc[st][v] * scale_log2;
+          mx = fmaxf(mx, x[st][v]);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        x[st][v] = exp2f(x[st][v] - m_use);
+        x[st][v] = __builtin_amdgcn_exp2f(x[st][v] - m_use);
         psum += x[st][v];
       }
     l_lane = l_lane * alpha + psum;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+    }
 
     // O^T += V^T P^T over two 32-key halves.  Reduction slot 8*lg + e maps to
     // key 32*hf + 4*lg + e (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4).
+    // Transpose-read addresses: lane (lr, lg) names key row base + lr/4 and
+    // columns 16*d + 4*(lr%4) .. +3.
+    const int trow = lg * 4 + (lr >> 2);
+    const int tcol = (lr & 3) * 4;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       u32x4_t pb;
@@ -233,15 +265,11 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
       pb[1] = pack2(x[2 * hf][2], x[2 * hf][3]);
       pb[2] = pack2(x[2 * hf + 1][0], x[2 * hf + 1][1]);
       pb[3] = pack2(x[2 * hf + 1][2], x[2 * hf + 1][3]);
-      const int r0 = hf * 32 + lg * 4;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
-        const int col = d * 16 + lr;
-        u32x4_t a;
-        a[0] = (uint32_t)vs[r0 + 0][col] | ((uint32_t)vs[r0 + 1][col] << 16);
-        a[1] = (uint32_t)vs[r0 + 2][col] | ((uint32_t)vs[r0 + 3][col] << 16);
-        a[2] = (uint32_t)vs[r0 + 16][col] | ((uint32_t)vs[r0 + 17][col] << 16);
-        a[3] = (uint32_t)vs[r0 + 18][col] | ((uint32_t)vs[r0 + 19][col] << 16);
+        const uint2 lo = read_tr(&vs[hf * 32 + trow][d * 16 + tcol]);
+        const uint2 hi = read_tr(&vs[hf * 32 + 16 + trow][d * 16 + tcol]);
+        const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
         oacc[d] = mfma(a, pb, oacc[d]);
       }
     }

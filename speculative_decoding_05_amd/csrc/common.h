@@ -53,4 +53,53 @@ __device__ inline int xcd_remap(int bid, int nblocks) {
   return (bid % 8) * n8 + bid / 8;
 }
 
+
+// ---------------------------------------------------------------------------
+// Wave reductions without LDS: four DPP steps combine the 16 lanes of each row
+// (partners lane^1, lane^2, then the half-row and row mirrors), after which
+// every lane holds its row's result; readlane fetches the four row results.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return (static_cast<uint64_t>(dpp<CTRL>(static_cast<uint32_t>(v >> 32))) << 32) | dpp<CTRL>(static_cast<uint32_t>(v));
+}
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int lane) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), lane));
+}
+__device__ __forceinline__ float readlanef(float v, int lane) {
+  return __builtin_bit_cast(float, readlane(__builtin_bit_cast(uint32_t, v), lane));
+}
+
+// max over the 16 lanes of each row (result in every lane of the row)
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp64<kDppXor1>(v); v = o > v ? o : v;
+  o = dpp64<kDppXor2>(v); v = o > v ? o : v;
+  o = dpp64<kDppHalfMirror>(v); v = o > v ? o : v;
+  o = dpp64<kDppMirror>(v); v = o > v ? o : v;
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = dpp<kDppXor1>(v); v = o > v ? o : v;
+  o = dpp<kDppXor2>(v); v = o > v ? o : v;
+  o = dpp<kDppHalfMirror>(v); v = o > v ? o : v;
+  o = dpp<kDppMirror>(v); v = o > v ? o : v;
+  const uint32_t a = readlane(v, 0), b = readlane(v, 16), c = readlane(v, 32), d = readlane(v, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
 }  // namespace medusa

@@ -3,12 +3,18 @@
 // At decode time the heads see one row per sequence (M <= 32), so both
 // projections are skinny GEMMs whose cost is streaming W1 / W2 from HBM once.
 // bf16 path: each wave owns 16*R output rows and a quarter of the reduction;
-// the weight slab is the MFMA A operand (v_mfma_f32_16x16x32_bf16, lane l
-// holds row l%16, reduction slice 8*(l/16)..+7), activations are the B
-// operand (M padded to 16*C columns), partial sums of the 4 waves are added in
-// LDS and the epilogue (SiLU + residual + bf16 rounding, or fp32 store) is
-// fused.  Weights are read with non-temporal loads so the small activation
-// block stays resident in L2.
+// the weight slab is the MFMA A operand (v_mfma_f32_16x16x32_bf16: lane l
+// holds row l%16, reduction slice 8*(l/16)..+7), activations are the B operand
+// (M padded to 16*C columns), partial sums of the 4 waves are added in LDS and
+// the epilogue (SiLU + residual + bf16 rounding, or fp32 store) is fused.
+//
+// Two weight layouts are accepted.  Row-major [K][N][H]: every load
+// instruction touches 16 rows x 64 bytes.  Packed (medusa_pack_weights): each
+// 16x32 A fragment is stored as one contiguous 1 KiB block in lane order, so
+// every load instruction of a wave reads 1 KiB of consecutive bytes and each
+// wave streams one contiguous region -- the layout reaches the HBM streaming
+// rate that the row-major pattern loses to scattered row segments.  Weights are
+// read with non-temporal loads so the small activation block stays in L2.
 #include "common.h"
 
 using namespace medusa;
@@ -21,7 +27,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kUnroll = 8;  // k-steps of 32 in flight per wave
 
 enum { EPI_RESBLOCK = 0, EPI_LOGITS = 1 };
 
@@ -31,7 +36,8 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 // out[head][m0+m][n] = sum_i W[head][n][i] * X[head][m0+m][i]   (m < Mg <= 16*C)
-template <int R, int C, int EPI>
+// R row tiles per wave, C column tiles, U k-steps of 32 loaded per wave before the MFMAs.
+template <int R, int C, int EPI, bool PACKED, int U>
 __global__ __launch_bounds__(kThreads) void head_gemm_bf16(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
     int H, int M_total, int m0, int Mg, int tiles_per_head, const uint16_t *__restrict__ resid,
@@ -43,15 +49,30 @@ __global__ __launch_bounds__(kThreads) void head_gemm_bf16(
   const int lr = lane & 15, lg = lane >> 4;
   const int kspan = H / kWaves;
   const int k0 = wave * kspan + lg * 8;
-  const uint16_t *Wh = W + (size_t)head * N * H;
+  const uint16_t *Wh = PACKED ? nullptr : W + (size_t)head * N * H;
   const uint16_t *Xh = X + (size_t)head * x_head_stride + (size_t)m0 * H;
 
+  // a_step: elements between the A fragments of consecutive k-steps
   const uint16_t *arow[R];
+  int a_step;
+  if (PACKED) {
+    // fragment (tile t, step s) at ((head*NT + t)*S + s)*512, lane l at +8*l
+    const int S = H / 32, NT = (N + 15) / 16;
+    const int t0 = n0 / 16;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    int n = n0 + r * 16 + lr;
-    n = n < N ? n : N - 1;  // ragged tail: read a valid row, result discarded
-    arow[r] = Wh + (size_t)n * H + k0;
+    for (int r = 0; r < R; ++r) {
+      const int t = t0 + r < NT ? t0 + r : NT - 1;  // ragged tail: valid tile, result discarded
+      arow[r] = W + (((size_t)head * NT + t) * S + wave * (kspan / 32)) * 512 + lane * 8;
+    }
+    a_step = 512;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int n = n0 + r * 16 + lr;
+      n = n < N ? n : N - 1;  // ragged tail: read a valid row, result discarded
+      arow[r] = Wh + (size_t)n * H + k0;
+    }
+    a_step = 32;
   }
   const uint16_t *brow[C];
   bool bval[C];
@@ -71,20 +92,20 @@ __global__ __launch_bounds__(kThreads) void head_gemm_bf16(
   const u32x4_t zero = {0u, 0u, 0u, 0u};
   const int steps = kspan / 32;
   int s = 0;
-  for (; s + kUnroll <= steps; s += kUnroll) {
-    u32x4_t a[kUnroll][R], b[kUnroll][C];
+  for (; s + U <= steps; s += U) {
+    u32x4_t a[U][R], b[U][C];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        a[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(arow[r] + (s + u) * 32));
+        a[u][r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(arow[r] + (s + u) * a_step));
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int c = 0; c < C; ++c)
         b[u][c] = bval[c] ? *reinterpret_cast<const u32x4_t *>(brow[c] + (s + u) * 32) : zero;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -93,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void head_gemm_bf16(
   for (; s < steps; ++s) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(arow[r] + s * 32));
+      const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(arow[r] + s * a_step));
 #pragma unroll
       for (int c = 0; c < C; ++c) {
         const u32x4_t b = bval[c] ? *reinterpret_cast<const u32x4_t *>(brow[c] + s * 32) : zero;
@@ -176,20 +197,54 @@ __global__ __launch_bounds__(256) void head_gemm_f32(const float *__restrict__ W
   }
 }
 
-template <int EPI>
+
+// Packed layout: Wp[k][t][s][l][e] = W[k][16t + l%16][32s + 8(l/16) + e]
+// (t < ceil(N/16), s < H/32, l < 64, e < 8; rows >= N are zero).
+// One thread moves one 16-byte lane slice.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__restrict__ W,
+                                                           uint16_t *__restrict__ Wp, int K, int N,
+                                                           int H) {
+  const int S = H / 32, NT = (N + 15) / 16;
+  const size_t total = (size_t)K * NT * S * 64;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int l = (int)(i % 64);
+  size_t f = i / 64;
+  const int s = (int)(f % S);
+  f /= S;
+  const int t = (int)(f % NT);
+  const int k = (int)(f / NT);
+  const int n = t * 16 + (l & 15);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < N) v = *reinterpret_cast<const u32x4_t *>(W + ((size_t)k * N + n) * H + s * 32 + (l >> 4) * 8);
+  *reinterpret_cast<u32x4_t *>(Wp + i * 8) = v;
+}
+
+template <int R, int C, int EPI, bool PACKED, int U>
+void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
+                int m0, int Mg, const uint16_t *resid, uint16_t *ob, float *of) {
+  const int tiles = (N + 16 * R - 1) / (16 * R);
+  hipLaunchKernelGGL((head_gemm_bf16<R, C, EPI, PACKED, U>), dim3(tiles * K), dim3(kThreads), 0, st, W, X, xhs, N,
+                     H, M, m0, Mg, tiles, resid, ob, of);
+}
+
+// Tiling by rows per group (measured on MI355X): up to 4 rows the B operand is
+// nearly free and one row tile with 16 k-steps in flight streams fastest;
+// with more rows two row tiles share each B fragment.
+template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  constexpr int R = EPI == EPI_LOGITS ? 2 : 1;
-  const int tiles = (N + 16 * R - 1) / (16 * R);
-  const dim3 grid(tiles * K);
+  const int steps = H / kWaves / 32;
   for (int m0 = 0; m0 < M; m0 += MEDUSA_MAX_HEADS_M) {
     const int Mg = M - m0 < MEDUSA_MAX_HEADS_M ? M - m0 : MEDUSA_MAX_HEADS_M;
-    if (Mg <= 16)
-      hipLaunchKernelGGL((head_gemm_bf16<R, 1, EPI>), grid, dim3(kThreads), 0, st, W, X, xhs, N, H,
-                         M, m0, Mg, tiles, resid, ob, of);
+    if (Mg <= 4 && steps % 16 == 0)
+      launch_one<1, 1, EPI, PACKED, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    else if (Mg <= 4)
+      launch_one<1, 1, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    else if (Mg <= 16)
+      launch_one<2, 1, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     else
-      hipLaunchKernelGGL((head_gemm_bf16<R, 2, EPI>), grid, dim3(kThreads), 0, st, W, X, xhs, N, H,
-                         M, m0, Mg, tiles, resid, ob, of);
+      launch_one<2, 2, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     medusa_status s = check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
     if (s != MEDUSA_OK) return s;
   }
@@ -226,7 +281,7 @@ extern "C" medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dty
     return fail(MEDUSA_ERR_ARG, "medusa_head_resblock: pointers must be 16-byte aligned");
   hipStream_t st = as_stream(stream);
   if (dt == MEDUSA_BF16)
-    return launch_bf16<EPI_RESBLOCK>(st, static_cast<const uint16_t *>(W1), static_cast<const uint16_t *>(h),
+    return launch_bf16<EPI_RESBLOCK, false>(st, static_cast<const uint16_t *>(W1), static_cast<const uint16_t *>(h),
                                      0, K, H, H, M, static_cast<const uint16_t *>(h),
                                      static_cast<uint16_t *>(r), nullptr);
   return launch_f32<EPI_RESBLOCK>(st, static_cast<const float *>(W1), static_cast<const float *>(h), 0,
@@ -245,7 +300,7 @@ extern "C" medusa_status medusa_head_vocab(medusa_stream_t stream, medusa_dtype 
   hipStream_t st = as_stream(stream);
   const long xhs = (long)M * H;
   if (dt == MEDUSA_BF16)
-    return launch_bf16<EPI_LOGITS>(st, static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(r),
+    return launch_bf16<EPI_LOGITS, false>(st, static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(r),
                                    xhs, K, V, H, M, nullptr, nullptr, logits);
   return launch_f32<EPI_LOGITS>(st, static_cast<const float *>(W2), static_cast<const float *>(r), xhs,
                                 K, V, H, M, nullptr, logits);
@@ -263,4 +318,62 @@ extern "C" medusa_status medusa_heads(medusa_stream_t stream, medusa_dtype dt, i
   s = medusa_head_resblock(stream, dt, K, M, H, h, W1, r);
   if (s != MEDUSA_OK) return s;
   return medusa_head_vocab(stream, dt, K, M, H, V, r, W2, logits);
+}
+
+// ---------------------------------------------------------------------------
+// packed-weight entry points (bf16)
+extern "C" size_t medusa_packed_weight_bytes(int K, int N, int H) {
+  if (K < 1 || N < 1 || H < 32 || H % 32 != 0) return 0;
+  return (size_t)K * ((N + 15) / 16) * (H / 32) * 512 * sizeof(uint16_t);
+}
+
+extern "C" medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H,
+                                             const void *W, void *Wp) {
+  if (K < 1 || N < 1 || H < 1) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: K=%d N=%d H=%d", K, N, H);
+  if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_pack_weights: needs H %% 128 == 0 (H=%d)", H);
+  if (!W || !Wp) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: NULL pointer");
+  if (!aligned16(W) || !aligned16(Wp)) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: pointers must be 16-byte aligned");
+  const size_t lanes = medusa_packed_weight_bytes(K, N, H) / 16;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint16_t *>(W), static_cast<uint16_t *>(Wp), K, N, H);
+  return check_launch("medusa_pack_weights");
+}
+
+extern "C" medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H,
+                                                     const void *h, const void *W1p, void *r) {
+  medusa_status s = check_common("medusa_head_resblock_packed", MEDUSA_BF16, K, M, H);
+  if (s != MEDUSA_OK) return s;
+  if (!h || !W1p || !r) return fail(MEDUSA_ERR_ARG, "medusa_head_resblock_packed: NULL pointer");
+  if (!aligned16(h) || !aligned16(W1p) || !aligned16(r))
+    return fail(MEDUSA_ERR_ARG, "medusa_head_resblock_packed: pointers must be 16-byte aligned");
+  return launch_bf16<EPI_RESBLOCK, true>(as_stream(stream), static_cast<const uint16_t *>(W1p),
+                                         static_cast<const uint16_t *>(h), 0, K, H, H, M,
+                                         static_cast<const uint16_t *>(h), static_cast<uint16_t *>(r), nullptr);
+}
+
+extern "C" medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V,
+                                                  const void *r, const void *W2p, float *logits) {
+  medusa_status s = check_common("medusa_head_vocab_packed", MEDUSA_BF16, K, M, H);
+  if (s != MEDUSA_OK) return s;
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: V=%d", V);
+  if (!r || !W2p || !logits) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: NULL pointer");
+  if (!aligned16(r) || !aligned16(W2p) || !aligned16(logits))
+    return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: pointers must be 16-byte aligned");
+  return launch_bf16<EPI_LOGITS, true>(as_stream(stream), static_cast<const uint16_t *>(W2p),
+                                       static_cast<const uint16_t *>(r), (long)M * H, K, V, H, M, nullptr,
+                                       nullptr, logits);
+}
+
+extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V,
+                                             const void *h, const void *W1p, const void *W2p, void *r,
+                                             float *logits) {
+  medusa_status s = check_common("medusa_heads_packed", MEDUSA_BF16, K, M, H);
+  if (s != MEDUSA_OK) return s;
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: V=%d", V);
+  if (!h || !W1p || !W2p || !r || !logits) return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: NULL pointer");
+  if (!aligned16(h) || !aligned16(W1p) || !aligned16(W2p) || !aligned16(r) || !aligned16(logits))
+    return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: pointers must be 16-byte aligned");
+  s = medusa_head_resblock_packed(stream, K, M, H, h, W1p, r);
+  if (s != MEDUSA_OK) return s;
+  return medusa_head_vocab_packed(stream, K, M, H, V, r, W2p, logits);
 }

@@ -3,21 +3,26 @@
 // Each element becomes a distinct 64-bit key: the order-preserving image of
 // the float (with -0.0 folded onto +0.0) in the high word and the bitwise
 // complement of the index in the low word, so that "larger key" means
-// "larger value, then smaller index" and every row has one exact answer.
-// Stage 1: a block of 256 threads holds a 2048-element chunk of a row in
-// registers and extracts its k largest keys by k rounds of block-wide max
-// (wave butterfly, then 4 wave results through LDS).  Stage 2: one block per
-// row merges the chunks' candidates the same way.
+// "larger value, then smaller index" and every row has exactly one answer.
+//
+// One block of 1024 threads holds a chunk of up to 32768 elements of a row in
+// registers.  The block's 64 groups of 16 lanes each find their largest key;
+// the k-th largest of those 64 group maxima, theta, is a lower bound of the
+// chunk's k-th largest key (k distinct keys are >= theta), so every answer is
+// >= theta.  The keys >= theta (typically a few dozen) are appended to LDS and
+// each is ranked exactly by counting the larger candidates; rank r < k goes to
+// output slot r.  Should the candidate set overflow LDS, the block falls back
+// to k rounds of block-wide max extraction.  Rows longer than one chunk write
+// per-chunk candidates that a second kernel merges by the same extraction.
 #include "common.h"
 
 using namespace medusa;
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;               // merge kernel
 constexpr int kPerThread = 8;
-constexpr int kChunk = kThreads * kPerThread;  // 2048
-constexpr int kMergeMax = kChunk;              // candidates stage 2 can hold
+constexpr int kMergeMax = kThreads * kPerThread;  // candidates the merge can hold
 
 __device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
   uint32_t u = __builtin_bit_cast(uint32_t, v);
@@ -34,8 +39,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int off) {
 
 // k rounds: each round finds the block-wide largest remaining key, removes it
 // from its (unique) owner and appends it to out[] (written by thread 0).
-template <int E>
-__device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_t (*s_wave)[4]) {
+template <int NT, int E>
+__device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_t (*s_wave)[NT / 64]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int round = 0; round < k; ++round) {
     uint64_t best = 0;
@@ -57,7 +62,7 @@ __device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_
     __syncthreads();
     uint64_t g = buf[0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) g = buf[i] > g ? buf[i] : g;
+    for (int i = 1; i < NT / 64; ++i) g = buf[i] > g ? buf[i] : g;
     if (g != 0 && best == g) {
 #pragma unroll
       for (int e = 0; e < E; ++e)
@@ -67,18 +72,119 @@ __device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_stage1(const float *__restrict__ logits, int V,
-                                                        int k, int nchunks, uint64_t *__restrict__ part) {
-  __shared__ uint64_t s_wave[2][4];
+constexpr int kFThreads = 1024;
+constexpr int kFE = 32;
+constexpr int kFChunk = kFThreads * kFE;  // 32768 elements per block
+constexpr int kCandMax = 1024;
+
+__global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict__ logits, int V, int k,
+                                                        int nchunks, int32_t *__restrict__ idx,
+                                                        float *__restrict__ val,
+                                                        uint64_t *__restrict__ part) {
+  __shared__ uint64_t s_gmax[kFThreads / 16];
+  __shared__ uint64_t s_cand[kCandMax];
+  __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
+  __shared__ uint64_t s_wave[2][kFThreads / 64];
+  __shared__ uint64_t s_theta;
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x;
   const int chunk = blockIdx.x, row = blockIdx.y;
   const float *z = logits + (size_t)row * V;
-  uint64_t keys[kPerThread];
+  const int base = chunk * kFChunk;
+  // values stay in registers as floats; keys are rebuilt from (value, index)
+  float v[kFE];
 #pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int i = chunk * kChunk + e * kThreads + threadIdx.x;
-    keys[e] = i < V ? make_key(z[i], static_cast<uint32_t>(i)) : 0ull;
+  for (int e = 0; e < kFE; ++e) {
+    const int i = base + e * kFThreads + tid;
+    v[e] = i < V ? z[i] : 0.f;
   }
-  block_extract(keys, k, part + ((size_t)row * nchunks + chunk) * k, s_wave);
+  auto key_of = [&](int e) -> uint64_t {
+    const int i = base + e * kFThreads + tid;
+    return i < V ? make_key(v[e], static_cast<uint32_t>(i)) : 0ull;
+  };
+  uint64_t m = 0;
+#pragma unroll
+  for (int e = 0; e < kFE; ++e) {
+    const uint64_t key = key_of(e);
+    m = key > m ? key : m;
+  }
+  m = row_max_u64(m);  // DPP steps within each 16-lane group
+  if ((tid & 15) == 0) s_gmax[tid >> 4] = m;
+  if (tid < MEDUSA_MAX_TOPK) s_out[tid] = 0ull;
+  if (tid == 0) {
+    s_theta = 1ull;  // fewer than k non-empty groups: every valid key is a candidate
+    s_cnt = 0;
+  }
+  __syncthreads();
+  if (tid < kFThreads / 16) {
+    const uint64_t v = s_gmax[tid];
+    int rank = 0;
+    for (int j = 0; j < kFThreads / 16; ++j) rank += s_gmax[j] > v ? 1 : 0;
+    if (v != 0ull && rank == k - 1) s_theta = v;
+  }
+  __syncthreads();
+  const uint64_t theta = s_theta;
+#pragma unroll
+  for (int e = 0; e < kFE; ++e) {
+    const uint64_t key = key_of(e);
+    if (key >= theta) {
+      const int p = atomicAdd(&s_cnt, 1);
+      if (p < kCandMax) s_cand[p] = key;
+    }
+  }
+  __syncthreads();
+  const int C = s_cnt;
+  if (C <= kCandMax) {
+    for (int i = tid; i < C; i += kFThreads) {
+      const uint64_t key = s_cand[i];
+      int rank = 0;
+      for (int j = 0; j < C; ++j) rank += s_cand[j] > key ? 1 : 0;
+      if (rank < k) s_out[rank] = key;
+    }
+  } else {
+    // overflow (rare: e.g. massive ties): k rounds of block-wide max; the
+    // values are re-read from memory so the fast path keeps its registers
+    const int wave = tid >> 6, lane = tid & 63;
+    uint32_t taken = 0u;
+    for (int round = 0; round < k; ++round) {
+      uint64_t best = 0;
+      int bi = 0;
+#pragma unroll 1
+      for (int e = 0; e < kFE; ++e) {
+        const int i = base + e * kFThreads + tid;
+        const uint64_t key = ((taken >> e) & 1u) || i >= V ? 0ull : make_key(z[i], static_cast<uint32_t>(i));
+        if (key > best) {
+          best = key;
+          bi = e;
+        }
+      }
+      uint64_t w = best;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(w, off);
+        w = o > w ? o : w;
+      }
+      uint64_t *buf = s_wave[round & 1];
+      if (lane == 0) buf[wave] = w;
+      __syncthreads();
+      uint64_t g = buf[0];
+#pragma unroll
+      for (int i = 1; i < kFThreads / 64; ++i) g = buf[i] > g ? buf[i] : g;
+      if (g != 0ull && best == g) taken |= 1u << bi;
+      if (tid == 0) s_out[round] = g;
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < k; j += kFThreads) {
+    const uint64_t key = s_out[j];
+    if (nchunks == 1) {
+      const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(key);
+      idx[(size_t)row * k + j] = static_cast<int32_t>(id);
+      if (val) val[(size_t)row * k + j] = z[id];
+    } else {
+      part[((size_t)row * nchunks + chunk) * k + j] = key;
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict__ logits, int V,
@@ -86,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict_
                                                         const uint64_t *__restrict__ part,
                                                         int32_t *__restrict__ idx,
                                                         float *__restrict__ val) {
-  __shared__ uint64_t s_wave[2][4];
+  __shared__ uint64_t s_wave[2][kThreads / 64];
   __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
   const int row = blockIdx.x;
   const int n = nchunks * k;
@@ -97,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict_
     const int i = e * kThreads + threadIdx.x;
     keys[e] = i < n ? p[i] : 0ull;
   }
-  block_extract(keys, k, s_out, s_wave);
+  block_extract<kThreads, kPerThread>(keys, k, s_out, s_wave);
   __syncthreads();
   for (int j = threadIdx.x; j < k; j += kThreads) {
     const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s_out[j]);
@@ -115,13 +221,14 @@ __global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restric
   tok[i] = j == 0 ? root[b] : topk_idx[((size_t)(depth[j] - 1) * B + b) * k + rank[j]];
 }
 
-inline int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
+inline int chunks_for(int V) { return (V + kFChunk - 1) / kFChunk; }
 
 }  // namespace
 
 extern "C" size_t medusa_topk_workspace(int R, int V, int k) {
   if (R < 1 || V < 1 || k < 1) return 0;
-  return (size_t)R * chunks_for(V) * k * sizeof(uint64_t);
+  const int nchunks = chunks_for(V);
+  return nchunks > 1 ? (size_t)R * nchunks * k * sizeof(uint64_t) : 0;
 }
 
 extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k,
@@ -130,7 +237,7 @@ extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k
   if (R < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "medusa_topk: R=%d V=%d", R, V);
   if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "medusa_topk: k=%d outside [1, V=%d]", k, V);
   if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: k=%d > %d", k, MEDUSA_MAX_TOPK);
-  if (!logits || !idx || !ws) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL pointer");
+  if (!logits || !idx) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL pointer");
   const int nchunks = chunks_for(V);
   if ((long)nchunks * k > kMergeMax)
     return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: V=%d with k=%d exceeds the merge capacity", V, k);
@@ -138,13 +245,15 @@ extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k
     return fail(MEDUSA_ERR_WORKSPACE, "medusa_topk: workspace %zu < %zu", ws_bytes,
                 medusa_topk_workspace(R, V, k));
   if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: R=%d > 65535", R);
+  const size_t need = medusa_topk_workspace(R, V, k);
+  if (need > 0 && !ws) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL workspace");
   hipStream_t st = as_stream(stream);
   uint64_t *part = static_cast<uint64_t *>(ws);
-  hipLaunchKernelGGL(topk_stage1, dim3(nchunks, R), dim3(kThreads), 0, st, logits, V, k, nchunks, part);
-  medusa_status s = check_launch("medusa_topk stage 1");
-  if (s != MEDUSA_OK) return s;
+  hipLaunchKernelGGL(topk_chunk, dim3(nchunks, R), dim3(kFThreads), 0, st, logits, V, k, nchunks, idx, val, part);
+  medusa_status s = check_launch("medusa_topk");
+  if (s != MEDUSA_OK || nchunks == 1) return s;
   hipLaunchKernelGGL(topk_stage2, dim3(R), dim3(kThreads), 0, st, logits, V, k, nchunks, part, idx, val);
-  return check_launch("medusa_topk stage 2");
+  return check_launch("medusa_topk merge");
 }
 
 extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B,

@@ -47,6 +47,12 @@ class Step:
         dev = device
         self.W1 = to_device(host["W1"], dev)
         self.W2 = to_device(host["W2"], dev)
+        self.packed = cfg.dtype == "bf16"
+        if self.packed:  # one-time reorder into the matrix-core fragment order
+            self.W1p = mb.PackedWeights(self.W1)
+            self.W2p = mb.PackedWeights(self.W2)
+            torch.cuda.synchronize()
+            del self.W1, self.W2
         self.root = to_device(host["root_tok"].astype(np.int32), dev)
         self.h = [to_device(host["h"], dev) for _ in range(copies)]
         self.q = [to_device(host["q"], dev) for _ in range(copies)]
@@ -77,10 +83,16 @@ class Step:
 
     # -- the stages -------------------------------------------------------------
     def heads(self, i=0):
-        mb.medusa_head_resblock(self.h[i], self.W1, self.r)
+        if self.packed:
+            mb.medusa_head_resblock_packed(self.h[i], self.W1p, self.r)
+        else:
+            mb.medusa_head_resblock(self.h[i], self.W1, self.r)
 
     def heads_vocab(self, i=0):
-        mb.medusa_head_vocab(self.r, self.W2, self.head_logits)
+        if self.packed:
+            mb.medusa_head_vocab_packed(self.r, self.W2p, self.head_logits)
+        else:
+            mb.medusa_head_vocab(self.r, self.W2, self.head_logits)
 
     def topk_and_tokens(self, i=0):
         mb.medusa_topk(self.head_logits, self.cfg.k, self.topk_idx, None, self.ws_topk)

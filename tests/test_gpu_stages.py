@@ -25,13 +25,16 @@ def head_inputs(dtype, K, M, H, V, seed):
     return h, W1, W2
 
 
-def run_heads(dtype, h, W1, W2):
+def run_heads(dtype, h, W1, W2, packed=False):
     K, V, H = W2.shape
     M = h.shape[0]
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
-    r = torch.empty((K, M, H), dtype=td, device="cuda")
+    r = torch.full((K, M, H), float("nan"), dtype=td, device="cuda")
     logits = torch.full((K, M, V), float("nan"), dtype=torch.float32, device="cuda")
-    mb.medusa_heads(dev(h), dev(W1), dev(W2), r, logits)
+    if packed:
+        mb.medusa_heads_packed(dev(h), mb.PackedWeights(dev(W1)), mb.PackedWeights(dev(W2)), r, logits)
+    else:
+        mb.medusa_heads(dev(h), dev(W1), dev(W2), r, logits)
     return host(r), host(logits)
 
 
@@ -45,10 +48,13 @@ def run_heads(dtype, h, W1, W2):
     ("f32", 2, 1, 256, 1000),       # the tiny fp32 configuration
     ("f32", 3, 9, 64, 130),
 ])
-def test_heads_parity(dtype, K, M, H, V):
-    say("heads", dtype, K, M, H, V)
+@pytest.mark.parametrize("packed", [False, True])
+def test_heads_parity(dtype, K, M, H, V, packed):
+    if packed and dtype != "bf16":
+        pytest.skip("packed weights are bf16 only")
+    say("heads", dtype, K, M, H, V, "packed" if packed else "row-major")
     h, W1, W2 = head_inputs(dtype, K, M, H, V, seed=K * 1000 + M)
-    r_g, lg_g = run_heads(dtype, h, W1, W2)
+    r_g, lg_g = run_heads(dtype, h, W1, W2, packed)
     f = synth.as_f64
     ref = oracle.medusa_heads(f(h), f(W1), f(W2), round_r_bf16=dtype == "bf16")
     r_ref = oracle.medusa_heads(f(h), f(W1), np.stack([np.eye(H)] * K), round_r_bf16=dtype == "bf16")
@@ -75,6 +81,27 @@ def test_zero_w1_reproduces_lm_head_bitwise(dtype):
     assert rel_err(lg_g[0], ref) <= TOL[dtype]
 
 
+def test_packed_equals_row_major_bitwise():
+    # the packed layout only changes where the weights sit, not the arithmetic
+    for K, M, H, V in [(4, 1, 512, 1000), (2, 20, 256, 333)]:
+        h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=M)
+        a = run_heads("bf16", h, W1, W2, packed=False)
+        b = run_heads("bf16", h, W1, W2, packed=True)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_pack_layout():
+    K, N, H = 2, 37, 128
+    W = store(rng(5).standard_normal((K, N, H)).astype(np.float32), "bf16")
+    Wp = host(mb.PackedWeights(dev(W)).data.view(torch.int16)).astype(np.int64) & 0xFFFF
+    NT, S = (N + 15) // 16, H // 32
+    Wp = Wp.reshape(K, NT, S, 64, 8)
+    for k, t, s_, l in [(0, 0, 0, 0), (1, 2, 3, 63), (1, 1, 2, 17), (0, 2, 1, 40)]:
+        n = 16 * t + l % 16
+        want = W[k, n, 32 * s_ + 8 * (l // 16):32 * s_ + 8 * (l // 16) + 8] if n < N else np.zeros(8)
+        assert Wp[k, t, s_, l].tolist() == np.asarray(want, np.int64).tolist()
+
+
 def test_heads_rows_and_heads_independent_bitwise():
     K, M, H, V = 3, 6, 256, 300
     h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=9)
@@ -95,6 +122,9 @@ def test_heads_rows_and_heads_independent_bitwise():
     (6, 1000, 2, "normal"), (3, 5003, 17, "normal"),
     (8, 32000, 10, "ties"), (4, 3000, 64, "ties"), (3, 50, 50, "normal"),
     (3, 4099, 5, "inf"), (2, 2048, 33, "zeros"),
+    (2, 50000, 10, "normal"), (2, 70001, 64, "normal"),          # several chunks + merge
+    (3, 32000, 10, "overflow"), (2, 32000, 64, "overflow"),      # candidate overflow fallback
+    (2, 32768, 10, "ties"), (64, 32000, 4, "normal"),
 ])
 def test_topk_bit_exact(R, V, k, kind):
     say("topk", R, V, k, kind)
@@ -106,6 +136,9 @@ def test_topk_bit_exact(R, V, k, kind):
         x[0, :] = -np.inf
         x[0, 4000] = 1.0
         x[1, ::2] = -np.inf
+    elif kind == "overflow":
+        # thread-strided copies of a descending ramp: the threshold admits thousands of keys
+        x = -(np.arange(V) % 1024).astype(np.float32)[None].repeat(R, 0)
     elif kind == "zeros":
         x[:] = 0.0
         x[0, ::3] = -0.0

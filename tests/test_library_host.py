@@ -128,7 +128,9 @@ def test_device_calls_validate_before_launch():
     assert s == mb.ERR_STATE
     assert mb.lib.medusa_topk(None, 2, 10, 11, fake, fake, None, fake, 1 << 20) == mb.ERR_ARG
     assert mb.lib.medusa_topk(None, 2, 100, 65, fake, fake, None, fake, 1 << 20) == mb.ERR_UNSUPPORTED
-    assert mb.lib.medusa_topk(None, 2, 100, 4, fake, fake, None, fake, 8) == mb.ERR_WORKSPACE
+    assert mb.lib.medusa_topk(None, 2, 40000, 4, fake, fake, None, fake, 8) == mb.ERR_WORKSPACE
+    assert mb.lib.medusa_pack_weights(None, 2, 10, 100, fake, fake) == mb.ERR_UNSUPPORTED
+    assert mb.lib.medusa_heads_packed(None, 4, 1, 256, 0, fake, fake, fake, fake, fake) == mb.ERR_ARG
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 100, 50, fake, fake, fake, fake, fake) == mb.ERR_UNSUPPORTED
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 50, fake, None, fake, fake, fake) == mb.ERR_ARG
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 50, P(0x1008), fake, fake, fake, fake) == mb.ERR_ARG
@@ -137,6 +139,7 @@ def test_device_calls_validate_before_launch():
 
 
 def test_workspace_sizes():
-    assert mb.medusa_topk_workspace(64, 32000, 10) == 64 * 16 * 10 * 8
+    assert mb.medusa_topk_workspace(64, 32000, 10) == 0              # one chunk per row
+    assert mb.medusa_topk_workspace(4, 70000, 10) == 4 * 3 * 10 * 8
     t = mb.Tree(oracle.dense_paths(2, 2), 2, 2)
     assert mb.typical_accept_workspace(t, 3, 1000) == 3 * 3 * 1 * 32   # 3 internal rows, 1 chunk
