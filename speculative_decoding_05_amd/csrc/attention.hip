@@ -41,8 +41,8 @@ constexpr int kKT = 64;        // keys per tile
 constexpr int kPadK = 8;       // row padding (bf16) of the K tile: 16 rows of a b128 read hit distinct banks
 constexpr int kPadV = 16;      // row padding (bf16) of the V tile: 8 rows of a transpose read hit distinct banks
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMinKeysPerSplit = 64;
-constexpr int kTargetBlocks = 1024;
+constexpr int kMinKeysPerSplit = 256;
+constexpr int kSplitTargetBlocks = 128;
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -65,9 +65,12 @@ struct Split {
   int nsplit, per_split;  // keys of the prefix per slice (multiple of kKT)
 };
 
+// Prefix slices per (b, head): measured on MI355X, split partials plus the
+// merge cost more than they gain once there are >= 128 (b, head, query-group)
+// blocks, so the prefix is split only below that (down to 256 keys a slice).
 inline Split choose_split(int B, int nh, int T, int L) {
   const long pairs = (long)B * nh * ((T + kQB - 1) / kQB);
-  int ns = (int)((kTargetBlocks + pairs - 1) / pairs);
+  int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
   const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
@@ -174,104 +177,115 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
-  TileRegs<DH> regs;
-  auto fetch = [&](int tile) {
+  // two register stages: tiles t+1 and t+2 are in flight while tile t is consumed
+  TileRegs<DH> regs0, regs1;
+  auto fetch = [&](TileRegs<DH> &r, int tile) {
     if (tile < ncache)
-      load_tile<DH>(regs, kc_bh, vc_bh, cache_stride, c0 + tile * kKT, c1);
+      load_tile<DH>(r, kc_bh, vc_bh, cache_stride, c0 + tile * kKT, c1);
     else
-      load_tile<DH>(regs, kt_bh, vt_bh, tree_stride, (tile - ncache) * kKT, T);
+      load_tile<DH>(r, kt_bh, vt_bh, tree_stride, (tile - ncache) * kKT, T);
   };
-  if (ntiles > 0) fetch(0);
+  auto consume = [&](int tile) {
+      const bool is_tree = tile >= ncache;
+      int kend;
+      uint64_t mword = ~0ull;
+      if (is_tree) {
+        const int tt = tile - ncache;
+        kend = T - tt * kKT;
+        mword = qvalid ? mask[(size_t)tq * W + tt] : 0ull;
+      } else {
+        kend = c1 - (c0 + tile * kKT);
+      }
 
-  for (int tile = 0; tile < ntiles; ++tile) {
+      // S^T for 4 sub-tiles of 16 keys: lane holds S[tq][key 16*st + 4*lg + v]
+      f32x4_t sacc[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&ks[st * 16 + lr][s * 32 + lg * 8]);
+          sacc[st] = mfma(a, qreg[s], sacc[st]);
+        }
+      }
+      // raw scores; the scale is folded into one FMA before exp2 (scale > 0 keeps the max)
+      float x[4][4];
+      float mx = -INFINITY;
+      if (is_tree || kend < kKT) {  // partial or tree tile: bounds and ancestor mask
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int key = st * 16 + lg * 4 + v;
+            const bool ok = key < kend && ((mword >> key) & 1ull);
+            x[st][v] = ok ? sacc[st][v] : -INFINITY;
+            mx = fmaxf(mx, x[st][v]);
+          }
+      } else {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            x[st][v] = sacc[st][v];
+            mx = fmaxf(mx, x[st][v]);
+          }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          x[st][v] = __builtin_amdgcn_exp2f(fmaf(x[st][v], scale_log2, -m_use));
+          psum += x[st][v];
+        }
+      l_lane = l_lane * alpha + psum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+      }
+
+      // O^T += V^T P^T over two 32-key halves.  Reduction slot 8*lg + e maps to
+      // key 32*hf + 4*lg + e (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4).
+      // Transpose-read addresses: lane (lr, lg) names key row base + lr/4 and
+      // columns 16*d + 4*(lr%4) .. +3.
+      const int trow = lg * 4 + (lr >> 2);
+      const int tcol = (lr & 3) * 4;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        u32x4_t pb;
+        pb[0] = pack2(x[2 * hf][0], x[2 * hf][1]);
+        pb[1] = pack2(x[2 * hf][2], x[2 * hf][3]);
+        pb[2] = pack2(x[2 * hf + 1][0], x[2 * hf + 1][1]);
+        pb[3] = pack2(x[2 * hf + 1][2], x[2 * hf + 1][3]);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          const uint2 lo = read_tr(&vs[hf * 32 + trow][d * 16 + tcol]);
+          const uint2 hi = read_tr(&vs[hf * 32 + 16 + trow][d * 16 + tcol]);
+          const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
+          oacc[d] = mfma(a, pb, oacc[d]);
+        }
+      }
+  };
+  if (ntiles > 0) fetch(regs0, 0);
+  if (ntiles > 1) fetch(regs1, 1);
+  for (int tile = 0; tile < ntiles; tile += 2) {
     __syncthreads();  // previous tile fully consumed
-    store_tile<DH>(regs, ks, vs);
+    store_tile<DH>(regs0, ks, vs);
     __syncthreads();
-    if (tile + 1 < ntiles) fetch(tile + 1);
-
-    const bool is_tree = tile >= ncache;
-    int kend;
-    uint64_t mword = ~0ull;
-    if (is_tree) {
-      const int tt = tile - ncache;
-      kend = T - tt * kKT;
-      mword = qvalid ? mask[(size_t)tq * W + tt] : 0ull;
-    } else {
-      kend = c1 - (c0 + tile * kKT);
-    }
-
-    // S^T for 4 sub-tiles of 16 keys: lane holds S[tq][key 16*st + 4*lg + v]
-    f32x4_t sacc[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&ks[st * 16 + lr][s * 32 + lg * 8]);
-        sacc[st] = mfma(a, qreg[s], sacc[st]);
-      }
-    }
-    float x[4][4];
-    float mx = -INFINITY;
-    if (is_tree || kend < kKT) {  // partial or tree tile: bounds and ancestor mask
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int key = st * 16 + lg * 4 + v;
-          const bool ok = key < kend && ((mword >> key) & 1ull);
-          x[st][v] = ok ? sacc[st][v] * scale_log2 : -INFINITY;
-          mx = fmaxf(mx, x[st][v]);
-        }
-    } else {
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          x[st][v] = sacc[st][v] * scale_log2;
-          mx = fmaxf(mx, x[st][v]);
-        }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        x[st][v] = __builtin_amdgcn_exp2f(x[st][v] - m_use);
-        psum += x[st][v];
-      }
-    l_lane = l_lane * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
-    }
-
-    // O^T += V^T P^T over two 32-key halves.  Reduction slot 8*lg + e maps to
-    // key 32*hf + 4*lg + e (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4).
-    // Transpose-read addresses: lane (lr, lg) names key row base + lr/4 and
-    // columns 16*d + 4*(lr%4) .. +3.
-    const int trow = lg * 4 + (lr >> 2);
-    const int tcol = (lr & 3) * 4;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4_t pb;
-      pb[0] = pack2(x[2 * hf][0], x[2 * hf][1]);
-      pb[1] = pack2(x[2 * hf][2], x[2 * hf][3]);
-      pb[2] = pack2(x[2 * hf + 1][0], x[2 * hf + 1][1]);
-      pb[3] = pack2(x[2 * hf + 1][2], x[2 * hf + 1][3]);
-#pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        const uint2 lo = read_tr(&vs[hf * 32 + trow][d * 16 + tcol]);
-        const uint2 hi = read_tr(&vs[hf * 32 + 16 + trow][d * 16 + tcol]);
-        const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
-        oacc[d] = mfma(a, pb, oacc[d]);
-      }
+    if (tile + 2 < ntiles) fetch(regs0, tile + 2);
+    consume(tile);
+    if (tile + 1 < ntiles) {
+      __syncthreads();
+      store_tile<DH>(regs1, ks, vs);
+      __syncthreads();
+      if (tile + 3 < ntiles) fetch(regs1, tile + 3);
+      consume(tile + 1);
     }
   }
 
