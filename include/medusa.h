@@ -191,6 +191,14 @@ medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, i
                                  int k, const int32_t *root_tok, const int32_t *topk_idx,
                                  int32_t *tree_tok);
 
+/* Both of the above in one pass: the per-head top-k of logits [K][B][V]
+ * (written to topk_idx [K][B][k]) and the node tokens tree_tok [B][T], each
+ * block that finishes a (head, sequence) row writing the tokens of the nodes
+ * that row feeds.  ws: medusa_topk_workspace(K*B, V, k) bytes. */
+medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B, int K, int V,
+                                      int k, const float *logits, const int32_t *root_tok,
+                                      int32_t *topk_idx, int32_t *tree_tok, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------------- */
 /* (3) Tree attention.  Paper summary, "基准/方法设计" (second component) and the
  *     FAQ on tree attention: all candidates share the prefix; node j attends

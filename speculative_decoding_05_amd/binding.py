@@ -54,6 +54,7 @@ SIGNATURES = {
     "medusa_tree_upload": (_i, [_p]),
     "medusa_tree_free": (None, [_p]),
     "medusa_tree_tokens": (_i, [_p, _p, _i, _i, _i, _p, _p, _p]),
+    "medusa_topk_tree_tokens": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz]),
     "tree_attention_workspace": (_sz, [_i, _p, _i, _i, _i, _i]),
     "tree_attention": (_i, [_p, _i, _p, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "typical_accept_workspace": (_sz, [_p, _i, _i]),
@@ -272,6 +273,17 @@ def medusa_tree_tokens(tree, root_tok, topk_idx, tree_tok):
     K, B, k = topk_idx.shape
     check(lib.medusa_tree_tokens(_stream(), tree.handle, B, K, k, _ptr(root_tok), _ptr(topk_idx),
                                  _ptr(tree_tok)))
+    return tree_tok
+
+
+def medusa_topk_tree_tokens(tree, logits, k, root_tok, topk_idx, tree_tok, ws=None):
+    """logits [K][B][V] -> topk_idx [K][B][k] and tree_tok [B][T] in one pass."""
+    _dev(logits, root_tok, topk_idx, tree_tok)
+    K, B, V = logits.shape
+    if ws is None:
+        ws = workspace(medusa_topk_workspace(K * B, V, k), logits.device)
+    check(lib.medusa_topk_tree_tokens(_stream(), tree.handle, B, K, V, k, _ptr(logits), _ptr(root_tok),
+                                      _ptr(topk_idx), _ptr(tree_tok), _ptr(ws), ws.numel()))
     return tree_tok
 
 

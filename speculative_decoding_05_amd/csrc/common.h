@@ -14,13 +14,14 @@ struct medusa_tree {
   std::vector<int32_t> parent, depth, rank, retrieve;
   std::vector<int32_t> internal;  // nodes with children, ascending
   std::vector<int32_t> slot;      // node -> index in `internal`, -1 for leaves
+  std::vector<int32_t> dstart;    // [depth_max + 2]: nodes of depth d are dstart[d] .. dstart[d+1]-1
   std::vector<uint64_t> mask;     // [T][W]
   // device copy (valid after upload)
   void *d_base = nullptr;
   int device = -1;
   const uint64_t *d_mask = nullptr;
   const int32_t *d_parent = nullptr, *d_depth = nullptr, *d_rank = nullptr;
-  const int32_t *d_internal = nullptr, *d_slot = nullptr;
+  const int32_t *d_internal = nullptr, *d_slot = nullptr, *d_dstart = nullptr;
 };
 
 namespace medusa {

@@ -192,6 +192,8 @@ extern "C" medusa_status medusa_build_tree(const int32_t *ranks, const int32_t *
     }
   t->n_internal = static_cast<int>(t->internal.size());
   t->depth_max = *std::max_element(t->depth.begin(), t->depth.end());
+  t->dstart.assign(t->depth_max + 2, t->T);  // nodes are sorted by depth
+  for (int j = t->T - 1; j >= 0; --j) t->dstart[t->depth[j]] = j;
   const int R = t->depth_max + 1;
   for (int j = 0; j < t->T; ++j)
     if (!has_child[j]) {
@@ -235,7 +237,7 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   if (t->d_base) return MEDUSA_OK;
   const size_t T = t->T;
   const size_t mask_b = T * t->W * sizeof(uint64_t);
-  const size_t ints = 4 * T + t->internal.size();
+  const size_t ints = 4 * T + t->internal.size() + t->dstart.size();
   const size_t bytes = mask_b + ints * sizeof(int32_t);
   std::vector<unsigned char> img(bytes);
   unsigned char *p = img.data();
@@ -247,6 +249,7 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   std::copy(t->rank.begin(), t->rank.end(), q + 2 * T);
   std::copy(t->slot.begin(), t->slot.end(), q + 3 * T);
   std::copy(t->internal.begin(), t->internal.end(), q + 4 * T);
+  std::copy(t->dstart.begin(), t->dstart.end(), q + 4 * T + t->internal.size());
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MEDUSA_ERR_HIP, "tree_upload: no HIP device");
   void *d = nullptr;
@@ -267,6 +270,7 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   t->d_rank = di + 2 * T;
   t->d_slot = di + 3 * T;
   t->d_internal = di + 4 * T;
+  t->d_dstart = di + 4 * T + t->internal.size();
   return MEDUSA_OK;
 }
 

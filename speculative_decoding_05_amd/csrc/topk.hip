@@ -72,6 +72,25 @@ __device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_
   }
 }
 
+// Optional tree-token scatter: the block that finishes row (head, b) writes the
+// tokens of every node at depth head+1 (its rank-th candidate), and the head-0
+// block also writes the root token.  Each node is written by exactly one block.
+struct TokenScatter {
+  int32_t *tree_tok;  // [B][T] or nullptr
+  const int32_t *rank, *dstart, *root;
+  int B, T, depth_max;
+};
+
+__device__ __forceinline__ void scatter_tokens(const TokenScatter &ts, int row, const uint64_t *s_out) {
+  if (!ts.tree_tok) return;
+  const int head = row / ts.B, b = row % ts.B;
+  if (head + 1 > ts.depth_max) return;
+  const int j0 = ts.dstart[head + 1], j1 = ts.dstart[head + 2];
+  for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x)
+    ts.tree_tok[(size_t)b * ts.T + j] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s_out[ts.rank[j]]));
+  if (head == 0 && threadIdx.x == 0) ts.tree_tok[(size_t)b * ts.T] = ts.root[b];
+}
+
 constexpr int kFThreads = 1024;
 constexpr int kFE = 32;
 constexpr int kFChunk = kFThreads * kFE;  // 32768 elements per block
@@ -80,7 +99,7 @@ constexpr int kCandMax = 1024;
 __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict__ logits, int V, int k,
                                                         int nchunks, int32_t *__restrict__ idx,
                                                         float *__restrict__ val,
-                                                        uint64_t *__restrict__ part) {
+                                                        uint64_t *__restrict__ part, TokenScatter ts) {
   __shared__ uint64_t s_gmax[kFThreads / 16];
   __shared__ uint64_t s_cand[kCandMax];
   __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
@@ -185,13 +204,14 @@ __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict_
       part[((size_t)row * nchunks + chunk) * k + j] = key;
     }
   }
+  if (nchunks == 1) scatter_tokens(ts, row, s_out);
 }
 
 __global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict__ logits, int V,
                                                         int k, int nchunks,
                                                         const uint64_t *__restrict__ part,
                                                         int32_t *__restrict__ idx,
-                                                        float *__restrict__ val) {
+                                                        float *__restrict__ val, TokenScatter ts) {
   __shared__ uint64_t s_wave[2][kThreads / 64];
   __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
   const int row = blockIdx.x;
@@ -210,6 +230,7 @@ __global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict_
     idx[(size_t)row * k + j] = static_cast<int32_t>(id);
     if (val) val[(size_t)row * k + j] = logits[(size_t)row * V + id];
   }
+  scatter_tokens(ts, row, s_out);
 }
 
 __global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restrict__ depth,
@@ -231,29 +252,47 @@ extern "C" size_t medusa_topk_workspace(int R, int V, int k) {
   return nchunks > 1 ? (size_t)R * nchunks * k * sizeof(uint64_t) : 0;
 }
 
-extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k,
-                                     const float *logits, int32_t *idx, float *val, void *ws,
-                                     size_t ws_bytes) {
-  if (R < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "medusa_topk: R=%d V=%d", R, V);
-  if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "medusa_topk: k=%d outside [1, V=%d]", k, V);
-  if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: k=%d > %d", k, MEDUSA_MAX_TOPK);
-  if (!logits || !idx) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL pointer");
+static medusa_status topk_launch(const char *who, hipStream_t st, int R, int V, int k, const float *logits,
+                                 int32_t *idx, float *val, void *ws, size_t ws_bytes, const TokenScatter &ts) {
+  if (R < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "%s: R=%d V=%d", who, R, V);
+  if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "%s: k=%d outside [1, V=%d]", who, k, V);
+  if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: k=%d > %d", who, k, MEDUSA_MAX_TOPK);
+  if (!logits || !idx) return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
   const int nchunks = chunks_for(V);
   if ((long)nchunks * k > kMergeMax)
-    return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: V=%d with k=%d exceeds the merge capacity", V, k);
-  if (ws_bytes < medusa_topk_workspace(R, V, k))
-    return fail(MEDUSA_ERR_WORKSPACE, "medusa_topk: workspace %zu < %zu", ws_bytes,
-                medusa_topk_workspace(R, V, k));
-  if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_topk: R=%d > 65535", R);
+    return fail(MEDUSA_ERR_UNSUPPORTED, "%s: V=%d with k=%d exceeds the merge capacity", who, V, k);
   const size_t need = medusa_topk_workspace(R, V, k);
-  if (need > 0 && !ws) return fail(MEDUSA_ERR_ARG, "medusa_topk: NULL workspace");
-  hipStream_t st = as_stream(stream);
+  if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, need);
+  if (need > 0 && !ws) return fail(MEDUSA_ERR_ARG, "%s: NULL workspace", who);
+  if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: R=%d > 65535", who, R);
   uint64_t *part = static_cast<uint64_t *>(ws);
-  hipLaunchKernelGGL(topk_chunk, dim3(nchunks, R), dim3(kFThreads), 0, st, logits, V, k, nchunks, idx, val, part);
-  medusa_status s = check_launch("medusa_topk");
+  hipLaunchKernelGGL(topk_chunk, dim3(nchunks, R), dim3(kFThreads), 0, st, logits, V, k, nchunks, idx, val, part, ts);
+  medusa_status s = check_launch(who);
   if (s != MEDUSA_OK || nchunks == 1) return s;
-  hipLaunchKernelGGL(topk_stage2, dim3(R), dim3(kThreads), 0, st, logits, V, k, nchunks, part, idx, val);
-  return check_launch("medusa_topk merge");
+  hipLaunchKernelGGL(topk_stage2, dim3(R), dim3(kThreads), 0, st, logits, V, k, nchunks, part, idx, val, ts);
+  return check_launch(who);
+}
+
+extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k, const float *logits,
+                                     int32_t *idx, float *val, void *ws, size_t ws_bytes) {
+  const TokenScatter none = {nullptr, nullptr, nullptr, nullptr, 1, 1, 0};
+  return topk_launch("medusa_topk", as_stream(stream), R, V, k, logits, idx, val, ws, ws_bytes, none);
+}
+
+extern "C" medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B, int K,
+                                                 int V, int k, const float *logits, const int32_t *root_tok,
+                                                 int32_t *topk_idx, int32_t *tree_tok, void *ws,
+                                                 size_t ws_bytes) {
+  medusa_status s = check_tree_on_device(t);
+  if (s != MEDUSA_OK) return s;
+  if (B < 1 || K < 1) return fail(MEDUSA_ERR_ARG, "medusa_topk_tree_tokens: B=%d K=%d", B, K);
+  if (!root_tok || !tree_tok) return fail(MEDUSA_ERR_ARG, "medusa_topk_tree_tokens: NULL pointer");
+  if (K < t->depth_max || k < t->k)
+    return fail(MEDUSA_ERR_SHAPE, "medusa_topk_tree_tokens: top-k block [K=%d][k=%d] smaller than the tree's [%d][%d]",
+                K, k, t->depth_max, t->k);
+  const TokenScatter ts = {tree_tok, t->d_rank, t->d_dstart, root_tok, B, t->T, t->depth_max};
+  return topk_launch("medusa_topk_tree_tokens", as_stream(stream), K * B, V, k, logits, topk_idx, nullptr, ws,
+                     ws_bytes, ts);
 }
 
 extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B,

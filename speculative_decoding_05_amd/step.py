@@ -95,8 +95,8 @@ class Step:
             mb.medusa_head_vocab(self.r, self.W2, self.head_logits)
 
     def topk_and_tokens(self, i=0):
-        mb.medusa_topk(self.head_logits, self.cfg.k, self.topk_idx, None, self.ws_topk)
-        mb.medusa_tree_tokens(self.tree, self.root, self.topk_idx, self.tree_tok)
+        mb.medusa_topk_tree_tokens(self.tree, self.head_logits, self.cfg.k, self.root, self.topk_idx,
+                                   self.tree_tok, self.ws_topk)
 
     def attention(self, i=0):
         mb.tree_attention(self.tree, self.q[i], self.kt[i], self.vt[i], self.kc[i], self.vc[i], self.attn,

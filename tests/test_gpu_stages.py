@@ -163,6 +163,26 @@ def test_tree_tokens_bit_exact():
     assert np.array_equal(host(out), oracle.tree_tokens(ot, root, idx))
 
 
+@pytest.mark.parametrize("K,k,B,V,paths", [
+    (4, 10, 3, 32000, "greedy64"), (5, 10, 2, 32000, "greedy64"),   # head 5 feeds no node
+    (4, 4, 2, 40000, "dense44"), (2, 2, 4, 1000, "dense22"),
+])
+def test_topk_tree_tokens_fused(K, k, B, V, paths):
+    pl = {"greedy64": oracle.greedy_paths(configs.acc_exact, 4, 63, 10),
+          "dense44": oracle.dense_paths(4, 4), "dense22": oracle.dense_paths(2, 2)}[paths]
+    ot = oracle.build_tree(pl, K, k)
+    t = mb.Tree(pl, K, k).upload()
+    g = rng(K * B + V)
+    x = g.standard_normal((K, B, V)).astype(np.float32)
+    root = g.integers(0, V, B).astype(np.int32)
+    idx = torch.full((K, B, k), -1, dtype=torch.int32, device="cuda")
+    tok = torch.full((B, t.T), -1, dtype=torch.int32, device="cuda")
+    mb.medusa_topk_tree_tokens(t, dev(x), k, dev(root), idx, tok)
+    ri, _ = oracle.topk_per_head(x.astype(np.float64), k)
+    assert np.array_equal(host(idx), ri)
+    assert np.array_equal(host(tok), oracle.tree_tokens(ot, root, ri))
+
+
 # ------------------------------------------------------------------ attention
 def attn_case(dtype, paths, K, k, B, nh, dh, L, seed, qscale=1.0):
     ot = oracle.build_tree(paths, K, k)
