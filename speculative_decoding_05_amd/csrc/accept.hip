@@ -1,6 +1,6 @@
 // Typical acceptance over the candidate tree.
 //
-// Row pass (one block per 4096-wide chunk of the verification row of a node
+// Row pass (one block per 4096- or 16384-wide chunk of the verification row of a node
 // that has children): every thread folds its 16 values into running
 // statistics of y = z / temperature -- max m, S = sum e^(y-m),
 // E = sum e^(y-m) (y-m) -- and the argmax of z (lowest index on ties); one
@@ -24,8 +24,9 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;                  // row pass
-constexpr int kVec = 4;                        // float4 per thread
-constexpr int kChunk = kThreads * kVec * 4;    // 4096 floats
+constexpr int kVecNarrow = 4;                  // float4 per thread: 4096-wide chunks
+constexpr int kVecWide = 16;                   // 16384-wide chunks when many rows (measured)
+constexpr long kWideRows = 2048;               // rows at which the wide chunks win
 constexpr int kScanThreads = 512;              // scan
 constexpr int kBatch = 8;                      // independent loads issued together
 constexpr float kLog2e = 1.4426950408889634f;
@@ -102,6 +103,7 @@ __device__ Stat block_reduce(Stat s, Stat *sh) {
   return r;
 }
 
+template <int VEC>
 __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restrict__ logits, int T,
                                                            int V, int n_internal,
                                                            const int32_t *__restrict__ internal,
@@ -111,12 +113,12 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
   const int chunk = blockIdx.x, slot = blockIdx.y, b = blockIdx.z;
   const int row = internal[slot];
   const float *z = logits + ((size_t)b * T + row) * V;
-  const int base = chunk * kChunk;
+  const int base = chunk * kThreads * VEC * 4;
   const bool vec_ok = (V % 4) == 0;
-  float val[kVec][4];
+  float val[VEC][4];
   Stat st = empty_stat();
 #pragma unroll
-  for (int u = 0; u < kVec; ++u) {
+  for (int u = 0; u < VEC; ++u) {
     const int i0 = base + (u * kThreads + threadIdx.x) * 4;
     if (vec_ok && i0 + 3 < V) {
       const f32x4_t f = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(z + i0));
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
   if (!greedy && st.av != -INFINITY) {
     st.m = st.av * inv_tau;  // max of y (tau > 0 keeps the order)
 #pragma unroll
-    for (int u = 0; u < kVec; ++u)
+    for (int u = 0; u < VEC; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float d = val[u][j] * inv_tau - st.m;  // -inf for padding
@@ -286,13 +288,14 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   if (tid == 0) next_tok[b] = st.ai;
 }
 
-inline int chunks_for(int V) { return (V + kChunk - 1) / kChunk; }
+inline int vec_for(int B, int n_internal) { return (long)B * n_internal >= kWideRows ? kVecWide : kVecNarrow; }
+inline int chunks_for(int V, int vec) { return (V + kThreads * vec * 4 - 1) / (kThreads * vec * 4); }
 
 }  // namespace
 
 extern "C" size_t typical_accept_workspace(const medusa_tree *t, int B, int V) {
   if (!t || B < 1 || V < 1) return 0;
-  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V) * sizeof(Part);
+  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V, vec_for(B, t->n_internal)) * sizeof(Part);
 }
 
 extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
@@ -312,13 +315,18 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
   const size_t need = typical_accept_workspace(t, B, V);
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = as_stream(stream);
-  const int nchunks = chunks_for(V);
+  const int vec = vec_for(B, t->n_internal);
+  const int nchunks = chunks_for(V, vec);
   const int greedy = temperature == 0.f;
   const float inv_tau = greedy ? 1.f : 1.f / temperature;
   Part *part = static_cast<Part *>(ws);
   if (t->n_internal > 0) {
-    hipLaunchKernelGGL(accept_rowpass, dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st, logits,
-                       t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
+    if (vec == kVecWide)
+      hipLaunchKernelGGL((accept_rowpass<kVecWide>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
+                         logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
+    else
+      hipLaunchKernelGGL((accept_rowpass<kVecNarrow>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
+                         logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
     s = check_launch("typical_accept row pass");
     if (s != MEDUSA_OK) return s;
   }

@@ -36,18 +36,19 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
 }
 
 // out[head][m0+m][n] = sum_i W[head][n][i] * X[head][m0+m][i]   (m < Mg <= 16*C)
-// R row tiles per wave, C column tiles, U k-steps of 32 loaded per wave before the MFMAs.
-template <int R, int C, int EPI, bool PACKED, int U>
-__global__ __launch_bounds__(kThreads) void head_gemm_bf16(
+// R row tiles per wave, C column tiles, U k-steps of 32 loaded per wave before
+// the MFMAs, NW waves per block splitting the reduction.
+template <int R, int C, int EPI, bool PACKED, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void head_gemm_bf16(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
     int H, int M_total, int m0, int Mg, int tiles_per_head, const uint16_t *__restrict__ resid,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
-  __shared__ float red[kWaves][16 * C][16 * R + 1];
+  __shared__ float red[NW][16 * C][16 * R + 1];
   const int head = blockIdx.x / tiles_per_head;
   const int n0 = (blockIdx.x % tiles_per_head) * 16 * R;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int kspan = H / kWaves;
+  const int kspan = H / NW;
   const int k0 = wave * kspan + lg * 8;
   const uint16_t *Wh = PACKED ? nullptr : W + (size_t)head * N * H;
   const uint16_t *Xh = X + (size_t)head * x_head_stride + (size_t)m0 * H;
@@ -132,11 +133,13 @@ __global__ __launch_bounds__(kThreads) void head_gemm_bf16(
       for (int v = 0; v < 4; ++v) red[wave][c * 16 + lr][r * 16 + lg * 4 + v] = acc[r][c][v];
   __syncthreads();
 
-  for (int e = threadIdx.x; e < 16 * C * 16 * R; e += kThreads) {
+  for (int e = threadIdx.x; e < 16 * C * 16 * R; e += 64 * NW) {
     const int m = e / (16 * R), nl = e % (16 * R);
     const int n = n0 + nl;
     if (m >= Mg || n >= N) continue;
-    const float v = red[0][m][nl] + red[1][m][nl] + red[2][m][nl] + red[3][m][nl];
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][m][nl];
     const size_t o = ((size_t)head * M_total + m0 + m) * N + n;
     if (EPI == EPI_LOGITS) {
       out_f32[o] = v;
@@ -220,31 +223,36 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__res
   *reinterpret_cast<u32x4_t *>(Wp + i * 8) = v;
 }
 
-template <int R, int C, int EPI, bool PACKED, int U>
+template <int R, int C, int EPI, bool PACKED, int U, int NW>
 void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
                 int m0, int Mg, const uint16_t *resid, uint16_t *ob, float *of) {
   const int tiles = (N + 16 * R - 1) / (16 * R);
-  hipLaunchKernelGGL((head_gemm_bf16<R, C, EPI, PACKED, U>), dim3(tiles * K), dim3(kThreads), 0, st, W, X, xhs, N,
-                     H, M, m0, Mg, tiles, resid, ob, of);
+  hipLaunchKernelGGL((head_gemm_bf16<R, C, EPI, PACKED, U, NW>), dim3(tiles * K), dim3(64 * NW), 0, st, W, X, xhs,
+                     N, H, M, m0, Mg, tiles, resid, ob, of);
 }
 
-// Tiling by rows per group (measured on MI355X): up to 4 rows the B operand is
-// nearly free and one row tile with 16 k-steps in flight streams fastest;
-// with more rows two row tiles share each B fragment.
+// Tiling by shape (measured on MI355X).  Vocabulary projection (N = V, many
+// tiles): up to 4 rows, one row tile per wave with 16 k-steps in flight;
+// more rows, two row tiles share each B fragment.  ResBlock (N = H, few
+// tiles): more waves per block split the reduction so enough loads are in
+// flight (16 waves x 4 k-steps for up to 4 rows, 8 waves otherwise).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  const int steps = H / kWaves / 32;
   for (int m0 = 0; m0 < M; m0 += MEDUSA_MAX_HEADS_M) {
     const int Mg = M - m0 < MEDUSA_MAX_HEADS_M ? M - m0 : MEDUSA_MAX_HEADS_M;
-    if (Mg <= 4 && steps % 16 == 0)
-      launch_one<1, 1, EPI, PACKED, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
+      launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
+      launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
+      launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     else if (Mg <= 4)
-      launch_one<1, 1, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+      launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     else if (Mg <= 16)
-      launch_one<2, 1, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+      launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     else
-      launch_one<2, 2, EPI, PACKED, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+      launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
     medusa_status s = check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
     if (s != MEDUSA_OK) return s;
   }
