@@ -1,8 +1,8 @@
 // Tree attention: every tree node attends to the prefix KV cache and to the
 // tree tokens on its own branch.
 //
-// bf16 path (one block = one sequence b, one head h, 64 tree queries, one
-// slice of the prefix).  The block streams its keys in tiles of 64: each tile
+// bf16 path (one block = one sequence b, one head h, 64 tree queries -- 128
+// when the tree has more than 64 tokens -- and one slice of the prefix).  The block streams its keys in tiles of 64: each tile
 // of K and V is read from HBM once with 16-byte coalesced loads (the next
 // tile is prefetched into registers while the current one is consumed) and
 // staged in LDS, where all 4 waves (16 queries each) use it.  Scores are
@@ -68,8 +68,12 @@ struct Split {
 // Prefix slices per (b, head): measured on MI355X, split partials plus the
 // merge cost more than they gain once there are >= 128 (b, head, query-group)
 // blocks, so the prefix is split only below that (down to 256 keys a slice).
+// Query tiles per wave: two once the tree has more than 64 tokens.
+inline int qtiles_for(int T) { return T > kQB ? 2 : 1; }
+
 inline Split choose_split(int B, int nh, int T, int L) {
-  const long pairs = (long)B * nh * ((T + kQB - 1) / kQB);
+  const int qb = kQB * qtiles_for(T);
+  const long pairs = (long)B * nh * ((T + qb - 1) / qb);
   int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
   const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
   if (ns > max_ns) ns = max_ns;
@@ -123,8 +127,12 @@ __device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)
   }
 }
 
-template <int DH>
-__global__ __launch_bounds__(kThreads) void tree_attn_bf16(
+// One block: sequence b, head h, 64*QT tree queries (QT tiles of 16 per wave),
+// one prefix slice.  With QT = 2 every K/V fragment read from LDS feeds two
+// MFMAs and the two tiles' softmax and MFMA streams interleave.
+// STAGES tiles are prefetched into registers ahead of the one being consumed.
+template <int DH, int QT, int STAGES>
+__global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
     int B, int nh, int T, int W, int L, float scale_log2, int qgroups, int nsplit, int per_split,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const uint64_t *__restrict__ mask,
@@ -145,16 +153,22 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int tq = qg * kQB + wave * 16 + lr;  // this lane's query (tree node)
-  const bool qvalid = tq < T;
+  int tq[QT];      // this lane's query (tree node) in each of its tiles
+  bool qvalid[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    tq[qt] = qg * kQB * QT + (wave * QT + qt) * 16 + lr;
+    qvalid[qt] = tq[qt] < T;
+  }
 
   // Q^T as the B operand: lane holds q[tq][32s + 8lg .. +8]
-  u32x4_t qreg[DS];
-  {
-    const uint16_t *qp = q + (((size_t)b * T + (qvalid ? tq : 0)) * nh + h) * DH + lg * 8;
+  u32x4_t qreg[QT][DS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const uint16_t *qp = q + (((size_t)b * T + (qvalid[qt] ? tq[qt] : 0)) * nh + h) * DH + lg * 8;
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      qreg[s] = qvalid ? *reinterpret_cast<const u32x4_t *>(qp + s * 32) : u32x4_t{0u, 0u, 0u, 0u};
+      qreg[qt][s] = qvalid[qt] ? *reinterpret_cast<const u32x4_t *>(qp + s * 32) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
   // key ranges: prefix slice [c0, c1), then (last slice only) the T tree keys
@@ -172,12 +186,17 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
   const uint16_t *kt_bh = kt + ((size_t)b * T * nh + h) * DH;
   const uint16_t *vt_bh = vt + ((size_t)b * T * nh + h) * DH;
 
-  f32x4_t oacc[DT];
+  f32x4_t oacc[QT][DT];
+  float m_run[QT], l_lane[QT];
 #pragma unroll
-  for (int d = 0; d < DT; ++d) oacc[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_lane = 0.f;
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int d = 0; d < DT; ++d) oacc[qt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[qt] = -INFINITY;
+    l_lane[qt] = 0.f;
+  }
 
-  // two register stages: tiles t+1 and t+2 are in flight while tile t is consumed
+  // register stages: tiles t+1 (and t+2) are in flight while tile t is consumed
   TileRegs<DH> regs0, regs1;
   auto fetch = [&](TileRegs<DH> &r, int tile) {
     if (tile < ncache)
@@ -186,130 +205,150 @@ __global__ __launch_bounds__(kThreads) void tree_attn_bf16(
       load_tile<DH>(r, kt_bh, vt_bh, tree_stride, (tile - ncache) * kKT, T);
   };
   auto consume = [&](int tile) {
-      const bool is_tree = tile >= ncache;
-      int kend;
-      uint64_t mword = ~0ull;
-      if (is_tree) {
-        const int tt = tile - ncache;
-        kend = T - tt * kKT;
-        mword = qvalid ? mask[(size_t)tq * W + tt] : 0ull;
-      } else {
-        kend = c1 - (c0 + tile * kKT);
-      }
+    const bool is_tree = tile >= ncache;
+    int kend;
+    uint64_t mword[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) mword[qt] = ~0ull;
+    if (is_tree) {
+      const int tt = tile - ncache;
+      kend = T - tt * kKT;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) mword[qt] = qvalid[qt] ? mask[(size_t)tq[qt] * W + tt] : 0ull;
+    } else {
+      kend = c1 - (c0 + tile * kKT);
+    }
+    const bool masked = is_tree || kend < kKT;
 
-      // S^T for 4 sub-tiles of 16 keys: lane holds S[tq][key 16*st + 4*lg + v]
-      f32x4_t sacc[4];
+    // S^T for 4 sub-tiles of 16 keys: lane holds S[tq][key 16*st + 4*lg + v]
+    f32x4_t sacc[QT][4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        sacc[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&ks[st * 16 + lr][s * 32 + lg * 8]);
-          sacc[st] = mfma(a, qreg[s], sacc[st]);
-        }
+      for (int qt = 0; qt < QT; ++qt) sacc[qt][st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(&ks[st * 16 + lr][s * 32 + lg * 8]);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) sacc[qt][st] = mfma(a, qreg[qt][s], sacc[qt][st]);
       }
-      // raw scores; the scale is folded into one FMA before exp2 (scale > 0 keeps the max)
-      float x[4][4];
+    }
+
+    // online softmax on raw scores; the scale is folded into one FMA before exp2
+    u32x4_t pb[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
       float mx = -INFINITY;
-      if (is_tree || kend < kKT) {  // partial or tree tile: bounds and ancestor mask
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 4; ++v) {
+          if (masked) {
             const int key = st * 16 + lg * 4 + v;
-            const bool ok = key < kend && ((mword >> key) & 1ull);
-            x[st][v] = ok ? sacc[st][v] : -INFINITY;
-            mx = fmaxf(mx, x[st][v]);
+            const bool ok = key < kend && ((mword[qt] >> key) & 1ull);
+            sacc[qt][st][v] = ok ? sacc[qt][st][v] : -INFINITY;
           }
-      } else {
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            x[st][v] = sacc[st][v];
-            mx = fmaxf(mx, x[st][v]);
-          }
-      }
+          mx = fmaxf(mx, sacc[qt][st][v]);
+        }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float m_new = fmaxf(m_run[qt], mx * scale_log2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
+      m_run[qt] = m_new;
       float psum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          x[st][v] = __builtin_amdgcn_exp2f(fmaf(x[st][v], scale_log2, -m_use));
-          psum += x[st][v];
+          sacc[qt][st][v] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][st][v], scale_log2, -m_use));
+          psum += sacc[qt][st][v];
         }
-      l_lane = l_lane * alpha + psum;
+      l_lane[qt] = l_lane[qt] * alpha + psum;
       if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+        for (int d = 0; d < DT; ++d) oacc[qt][d] *= alpha;
       }
-
-      // O^T += V^T P^T over two 32-key halves.  Reduction slot 8*lg + e maps to
-      // key 32*hf + 4*lg + e (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4).
-      // Transpose-read addresses: lane (lr, lg) names key row base + lr/4 and
-      // columns 16*d + 4*(lr%4) .. +3.
-      const int trow = lg * 4 + (lr >> 2);
-      const int tcol = (lr & 3) * 4;
+      // P^T B operands: reduction slot 8*lg + e maps to key 32*hf + 4*lg + e
+      // (e < 4) and 32*hf + 16 + 4*lg + (e - 4) (e >= 4)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        u32x4_t pb;
-        pb[0] = pack2(x[2 * hf][0], x[2 * hf][1]);
-        pb[1] = pack2(x[2 * hf][2], x[2 * hf][3]);
-        pb[2] = pack2(x[2 * hf + 1][0], x[2 * hf + 1][1]);
-        pb[3] = pack2(x[2 * hf + 1][2], x[2 * hf + 1][3]);
-#pragma unroll
-        for (int d = 0; d < DT; ++d) {
-          const uint2 lo = read_tr(&vs[hf * 32 + trow][d * 16 + tcol]);
-          const uint2 hi = read_tr(&vs[hf * 32 + 16 + trow][d * 16 + tcol]);
-          const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
-          oacc[d] = mfma(a, pb, oacc[d]);
-        }
+        pb[qt][hf][0] = pack2(sacc[qt][2 * hf][0], sacc[qt][2 * hf][1]);
+        pb[qt][hf][1] = pack2(sacc[qt][2 * hf][2], sacc[qt][2 * hf][3]);
+        pb[qt][hf][2] = pack2(sacc[qt][2 * hf + 1][0], sacc[qt][2 * hf + 1][1]);
+        pb[qt][hf][3] = pack2(sacc[qt][2 * hf + 1][2], sacc[qt][2 * hf + 1][3]);
       }
+    }
+
+    // O^T += V^T P^T; V^T fragments by transpose read: lane (lr, lg) names key
+    // row base + lr/4 and columns 16*d + 4*(lr%4) .. +3
+    const int trow = lg * 4 + (lr >> 2);
+    const int tcol = (lr & 3) * 4;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const uint2 lo = read_tr(&vs[hf * 32 + trow][d * 16 + tcol]);
+        const uint2 hi = read_tr(&vs[hf * 32 + 16 + trow][d * 16 + tcol]);
+        const u32x4_t a = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) oacc[qt][d] = mfma(a, pb[qt][hf], oacc[qt][d]);
+      }
+    }
   };
-  if (ntiles > 0) fetch(regs0, 0);
-  if (ntiles > 1) fetch(regs1, 1);
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    __syncthreads();  // previous tile fully consumed
-    store_tile<DH>(regs0, ks, vs);
-    __syncthreads();
-    if (tile + 2 < ntiles) fetch(regs0, tile + 2);
-    consume(tile);
-    if (tile + 1 < ntiles) {
+  if (STAGES == 2) {
+    if (ntiles > 0) fetch(regs0, 0);
+    if (ntiles > 1) fetch(regs1, 1);
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      __syncthreads();  // previous tile fully consumed
+      store_tile<DH>(regs0, ks, vs);
       __syncthreads();
-      store_tile<DH>(regs1, ks, vs);
+      if (tile + 2 < ntiles) fetch(regs0, tile + 2);
+      consume(tile);
+      if (tile + 1 < ntiles) {
+        __syncthreads();
+        store_tile<DH>(regs1, ks, vs);
+        __syncthreads();
+        if (tile + 3 < ntiles) fetch(regs1, tile + 3);
+        consume(tile + 1);
+      }
+    }
+  } else {
+    if (ntiles > 0) fetch(regs0, 0);
+    for (int tile = 0; tile < ntiles; ++tile) {
       __syncthreads();
-      if (tile + 3 < ntiles) fetch(regs1, tile + 3);
-      consume(tile + 1);
+      store_tile<DH>(regs0, ks, vs);
+      __syncthreads();
+      if (tile + 1 < ntiles) fetch(regs0, tile + 1);
+      consume(tile);
     }
   }
 
-  float l_tot = l_lane + __shfl_xor(l_lane, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!qvalid) return;
-  // lane holds O[tq][16*d + 4*lg + v]
-  if (nsplit == 1) {
-    const float inv = 1.f / l_tot;
-    uint16_t *op = out + (((size_t)b * T + tq) * nh + h) * DH + lg * 4;
 #pragma unroll
-    for (int d = 0; d < DT; ++d) {
-      uint2 w;
-      w.x = pack2(oacc[d][0] * inv, oacc[d][1] * inv);
-      w.y = pack2(oacc[d][2] * inv, oacc[d][3] * inv);
-      *reinterpret_cast<uint2 *>(op + d * 16) = w;
+  for (int qt = 0; qt < QT; ++qt) {
+    float l_tot = l_lane[qt] + __shfl_xor(l_lane[qt], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!qvalid[qt]) continue;
+    // lane holds O[tq][16*d + 4*lg + v]
+    if (nsplit == 1) {
+      const float inv = 1.f / l_tot;
+      uint16_t *op = out + (((size_t)b * T + tq[qt]) * nh + h) * DH + lg * 4;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        uint2 w;
+        w.x = pack2(oacc[qt][d][0] * inv, oacc[qt][d][1] * inv);
+        w.y = pack2(oacc[qt][d][2] * inv, oacc[qt][d][3] * inv);
+        *reinterpret_cast<uint2 *>(op + d * 16) = w;
+      }
+    } else {
+      const size_t row = (((size_t)split * B + b) * nh + h) * T + tq[qt];
+      float *op = ws_o + row * DH + lg * 4;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+        *reinterpret_cast<float4 *>(op + d * 16) =
+            make_float4(oacc[qt][d][0], oacc[qt][d][1], oacc[qt][d][2], oacc[qt][d][3]);
+      if (lg == 0) ws_ml[row] = make_float2(m_run[qt], l_tot);
     }
-  } else {
-    const size_t row = (((size_t)split * B + b) * nh + h) * T + tq;
-    float *op = ws_o + row * DH + lg * 4;
-#pragma unroll
-    for (int d = 0; d < DT; ++d)
-      *reinterpret_cast<float4 *>(op + d * 16) = make_float4(oacc[d][0], oacc[d][1], oacc[d][2], oacc[d][3]);
-    if (lg == 0) ws_ml[row] = make_float2(m_run, l_tot);
   }
 }
 
@@ -441,12 +480,12 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
   }
 }
 
-template <int DH>
+template <int DH, int QT>
 medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, int L, float scale,
                           const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                           const void *v_cache, void *out, void *ws) {
   const Split sp = choose_split(B, nh, t->T, L);
-  const int qgroups = (t->T + kQB - 1) / kQB;
+  const int qgroups = (t->T + kQB * QT - 1) / (kQB * QT);
   const long nblocks = (long)B * nh * qgroups * sp.nsplit;
   if (nblocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: grid too large");
   float *ws_o = nullptr;
@@ -455,7 +494,7 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, i
     ws_o = static_cast<float *>(ws);
     ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
   }
-  hipLaunchKernelGGL((tree_attn_bf16<DH>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
+  hipLaunchKernelGGL((tree_attn_bf16<DH, QT, QT == 1 ? 2 : 1>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
                      t->W, L, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
@@ -513,9 +552,14 @@ extern "C" medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt,
   if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "tree_attention: workspace must be 16-byte aligned");
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)dh) : scale;
   hipStream_t st = as_stream(stream);
-  if (dt == MEDUSA_BF16)
-    return dh == 128 ? launch_bf16<128>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
-                     : launch_bf16<64>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+  if (dt == MEDUSA_BF16) {
+    const bool two = qtiles_for(t->T) == 2;
+    if (dh == 128)
+      return two ? launch_bf16<128, 2>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+                 : launch_bf16<128, 1>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+    return two ? launch_bf16<64, 2>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+               : launch_bf16<64, 1>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+  }
   return dh == 128 ? launch_f32<128>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out)
                    : launch_f32<64>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out);
 }
