@@ -110,15 +110,28 @@ __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict_
   const int chunk = blockIdx.x, row = blockIdx.y;
   const float *z = logits + (size_t)row * V;
   const int base = chunk * kFChunk;
-  // values stay in registers as floats; keys are rebuilt from (value, index)
+  // values stay in registers as floats; keys are rebuilt from (value, index).
+  // Element e of this thread is index base + (e/4)*4096 + 4*tid + e%4, read
+  // as float4 when the row allows it.
   float v[kFE];
+  const bool vec = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
 #pragma unroll
-  for (int e = 0; e < kFE; ++e) {
-    const int i = base + e * kFThreads + tid;
-    v[e] = i < V ? z[i] : 0.f;
+  for (int g = 0; g < kFE / 4; ++g) {
+    const int i0 = base + g * 4 * kFThreads + 4 * tid;
+    if (vec && i0 + 3 < V) {
+      const float4 f = *reinterpret_cast<const float4 *>(z + i0);
+      v[4 * g] = f.x;
+      v[4 * g + 1] = f.y;
+      v[4 * g + 2] = f.z;
+      v[4 * g + 3] = f.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 * g + j] = i0 + j < V ? z[i0 + j] : 0.f;
+    }
   }
+  auto index_of = [&](int e) { return base + (e >> 2) * 4 * kFThreads + 4 * tid + (e & 3); };
   auto key_of = [&](int e) -> uint64_t {
-    const int i = base + e * kFThreads + tid;
+    const int i = index_of(e);
     return i < V ? make_key(v[e], static_cast<uint32_t>(i)) : 0ull;
   };
   uint64_t m = 0;
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict_
       int bi = 0;
 #pragma unroll 1
       for (int e = 0; e < kFE; ++e) {
-        const int i = base + e * kFThreads + tid;
+        const int i = index_of(e);
         const uint64_t key = ((taken >> e) & 1u) || i >= V ? 0ull : make_key(z[i], static_cast<uint32_t>(i));
         if (key > best) {
           best = key;
