@@ -324,3 +324,79 @@ def test_accept_uniform_rows():
     gpu = run_accept(t, logits, tok, 0.9, 0.3, 1.0)
     assert np.allclose(gpu["row_thr"][:, 0], 0.3 / 640, rtol=1e-5)
     assert (gpu["accept_len"] == 2).all() and (gpu["best"] == 3).all() and (gpu["next_tok"] == 0).all()
+
+
+# ------------------------------------------------------------------ robustness
+def random_tree(seed, K, k, n):
+    g = rng(seed)
+    paths, frontier = set(), [(i,) for i in range(k)]
+    while frontier and len(paths) < n:
+        p = frontier.pop(int(g.integers(len(frontier))))
+        paths.add(p)
+        if len(p) < K:
+            frontier.extend(p + (i,) for i in range(k))
+    order = [list(p) for p in paths]
+    g.shuffle(order)
+    return order
+
+
+@pytest.mark.parametrize("seed,K,k,n", [(1, 5, 3, 90), (2, 3, 8, 150), (3, 6, 2, 40), (4, 4, 6, 300)])
+def test_random_trees_end_to_end(seed, K, k, n):
+    paths = random_tree(seed, K, k, n)
+    say("random tree", seed, "T =", len(paths) + 1)
+    ot = oracle.build_tree(paths, K, k)
+    t = mb.Tree(paths, K, k).upload()
+    assert np.array_equal(t.mask, ot["mask"])
+    B, V, nh, dh, L = 3, 3000, 2, 128, 150
+    g = rng(seed + 10)
+    # candidate tokens via the fused top-k on logits fed to both sides
+    x = g.standard_normal((K, B, V)).astype(np.float32)
+    root = g.integers(0, V, B).astype(np.int32)
+    idx = torch.empty((K, B, k), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, t.T), dtype=torch.int32, device="cuda")
+    mb.medusa_topk_tree_tokens(t, dev(x), k, dev(root), idx, tok)
+    ri, _ = oracle.topk_per_head(x.astype(np.float64), k)
+    tok_o = oracle.tree_tokens(ot, root, ri)
+    assert np.array_equal(host(tok), tok_o)
+    # attention
+    mk = lambda shape: store(g.standard_normal(shape).astype(np.float32), "bf16")
+    q, kt, vt = mk((B, t.T, nh, dh)), mk((B, t.T, nh, dh)), mk((B, t.T, nh, dh))
+    kc, vc = mk((B, nh, L, dh)), mk((B, nh, L, dh))
+    got = run_attn("bf16", t, q, kt, vt, kc, vc)
+    f = synth.as_f64
+    check_attn("bf16", got, oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot))
+    # acceptance on planted logits
+    vl = synth.verification_logits(500 + seed, V, ot["parent"], ot["depth"], ot["rank"], ri, root,
+                                   configs.acc_float, k)
+    ref = oracle.typical_accept(vl.astype(np.float64), tok_o, ot, 0.09, 0.3, 1.0)
+    check_accept(ot, vl, tok_o, ref, run_accept(t, vl, tok_o, 0.09, 0.3, 1.0))
+
+
+def test_out_of_range_tokens_never_accepted():
+    ot, t, tok, logits = accept_case(oracle.dense_paths(2, 2), 2, 2, 2, 400, seed=8)
+    logits = np.zeros_like(logits)            # uniform rows: every in-range candidate passes
+    bad = tok.copy()
+    bad[0, 1] = 400                           # node (0,): id == V
+    bad[1, 2] = -5                            # node (1,): negative id
+    gpu = run_accept(t, logits, bad, 0.9, 0.3, 1.0)
+    assert gpu["cand_p"][0, 1] == 0.0 and gpu["cand_p"][1, 2] == 0.0
+    # sequence 0 loses branch (0,) and continues through (1,): best is (1,0) = node 5
+    assert gpu["best"].tolist() == [5, 3] and gpu["accept_len"].tolist() == [2, 2]
+
+
+def test_whole_step_is_deterministic():
+    from speculative_decoding_05_amd import step as st
+    cfg = configs.CONFIGS["tiny_f32"]
+    tree = st.build_tree(cfg)
+    hostin = st.host_inputs(cfg, tree.T)
+    s = st.Step(cfg, tree, hostin)
+    s.heads(); s.heads_vocab(); s.topk_and_tokens()
+    vl = st.verify_logits_for(cfg, tree, host(s.topk_idx), hostin["root_tok"])
+    s.set_verify_logits(vl)
+    outs = []
+    for _ in range(2):
+        s.run()
+        outs.append([host(x).copy() for x in (s.head_logits, s.topk_idx, s.tree_tok, s.attn, s.accept_len,
+                                               s.best, s.next_tok, s.accepted)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
