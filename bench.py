@@ -86,6 +86,41 @@ def counted_traffic(workload):
     return rec["bytes_per_launch"]
 
 
+def verify_pass(s, reps):
+    """The dense contractions at the verify-pass shape (M = B*T rows): Medusa
+    heads over every tree node and the LM head over the attention output.
+    Times each with HIP events on the launch stream; matrix-core utilisation
+    against the dense bf16 peak."""
+    import torch
+    from speculative_decoding_05_amd import step as st
+    cfg = s.cfg
+    vp = st.VerifyPass(s, seed=cfg.cfg_id)
+    M, H, V, K = vp.M, cfg.H, cfg.V, cfg.K
+    flops = {"heads_resblock": 2.0 * K * M * H * H, "heads_vocab": 2.0 * K * M * H * V,
+             "lm_head": 2.0 * M * H * V}
+    fns = {"heads_resblock": vp.heads_resblock, "heads_vocab": vp.heads_vocab, "lm_head": vp.lm_head}
+    out = {"rows": M, "us": {}, "tflops": {}, "mfma_frac": {}}
+    for name, fn in fns.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / reps
+        out["us"][name] = us
+        out["tflops"][name] = flops[name] / (us * 1e-6) / 1e12
+        out["mfma_frac"][name] = flops[name] / (us * 1e-6) / BF16_PEAK
+    tot_f, tot_us = sum(flops.values()), sum(out["us"].values())
+    out["total"] = {"us": tot_us, "tflops": tot_f / (tot_us * 1e-6) / 1e12,
+                    "mfma_frac": tot_f / (tot_us * 1e-6) / BF16_PEAK}
+    del vp
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(nbytes):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -143,6 +178,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="bytes of rotated per-step inputs")
     ap.add_argument("--copy-probe", type=int, default=0, help="only copy this many bytes (counter calibration)")
+    ap.add_argument("--verify-reps", type=int, default=5,
+                    help="repetitions of each verify-pass contraction (0: skip)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the vocabulary projection with events on every n-th timed step")
     args = ap.parse_args()
@@ -258,6 +295,9 @@ def main():
                      "bytes_per_launch": vocab_bytes, "avg_launch_us": vocab_ms * 1e3,
                      "launches_timed": len(ev)},
     }
+    if cfg.dtype == "bf16" and args.verify_reps > 0:
+        print("[bench] verify-pass contractions (M = B*T rows)", file=sys.stderr, flush=True)
+        res["verify_pass"] = verify_pass(s, args.verify_reps)
     print(f"[bench] {ms_step * 1e3:.1f} us/step; stages {json.dumps({k: round(v, 1) for k, v in stage_us.items()})}",
           file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:

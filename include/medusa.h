@@ -62,7 +62,7 @@ typedef struct medusa_tree medusa_tree;   /* opaque candidate tree */
 /* Limits checked by the calls below. */
 #define MEDUSA_MAX_TOPK 64        /* k of medusa_topk                         */
 #define MEDUSA_MAX_TREE 1024      /* tree tokens T, root included             */
-#define MEDUSA_MAX_HEADS_M 32     /* rows per medusa_heads launch group       */
+#define MEDUSA_MAX_HEADS_M 32     /* most rows of the weight-streaming kernel */
 
 const char *medusa_last_error(void);      /* thread-local text of the last non-OK status */
 int medusa_abi_version(void);
@@ -82,9 +82,13 @@ int medusa_abi_version(void);
  *  W2     [K][V][H]    device, dt       row = vocabulary entry
  *  r      [K][M][H]    device, dt       output of medusa_head_resblock
  *  logits [K][M][V]    device, float    output
- *  Limits: H % 128 == 0 for bf16 (H % 4 == 0 for f32); 1 <= M; rows are
- *  processed in groups of MEDUSA_MAX_HEADS_M (each group streams the weights
- *  once).  Errors: ERR_ARG (NULL, misaligned), ERR_UNSUPPORTED (H), ERR_HIP.
+ *  Limits: H % 128 == 0 for bf16 (H % 4 == 0 for f32); 1 <= M.  bf16 with
+ *  M <= MEDUSA_MAX_HEADS_M (decode: one row per sequence) streams the weights
+ *  once; larger M (the verify-pass shape, every tree node of every sequence,
+ *  M = B*T; or the backbone LM head over those rows, a head with W1 = 0) runs
+ *  a block-tiled matrix-core GEMM, which needs one head's weights and one
+ *  head's M x H activations to span less than 4 GiB each.
+ *  Errors: ERR_ARG (NULL, misaligned), ERR_UNSUPPORTED (H, 4 GiB), ERR_HIP.
  */
 medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dtype dt, int K, int M, int H,
                                    const void *h, const void *W1, void *r);

@@ -4,7 +4,7 @@ Only the test-suite, the smoke check and the bench's CPU-baseline leg may
 import this package.  It shares no code with the HIP library.
 """
 from .medusa import (  # noqa: F401
-    TreeError, bf16_round, medusa_heads, medusa_topk, dense_paths,
+    TreeError, bf16_round, medusa_heads, verification_logits, medusa_topk, dense_paths,
     greedy_paths, validate_paths, build_tree, ancestors, tree_positions,
     tree_tokens, tree_attention, row_distribution, typical_accept,
     topk_per_head, step,

@@ -94,6 +94,22 @@ def medusa_heads(h, W1, W2, round_r_bf16=False):
     return logits
 
 
+def verification_logits(x, W_lm):
+    """The backbone's logits at every tree node: its LM head applied to the
+    node's hidden state.  [P3] "基准/方法设计" gives the LM head as the W1 = 0
+    case of the head formula (SiLU(0) = 0, so r = h), i.e. a plain projection
+        z[b][t][v] = sum_i W_lm[v][i] x[b][t][i].
+    x [B][T][H], W_lm [V][H].  Reading: the hidden state handed to the LM head
+    is whatever the caller supplies (here, the tree-attention output of the
+    node with heads concatenated); the backbone layers between attention and
+    the LM head are outside this path.  Returns float64 [B][T][V].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W_lm = np.asarray(W_lm, dtype=np.float64)
+    B, T, H = x.shape
+    return (x.reshape(B * T, H) @ W_lm.T).reshape(B, T, W_lm.shape[0])
+
+
 # ----------------------------------------------------------------------------
 # (2) per-head top-k  -- [P2] "推理算法 / 候选生成", "超参数调优指南 / 每头 Top-K"
 # ----------------------------------------------------------------------------

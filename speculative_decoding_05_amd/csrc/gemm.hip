@@ -1,0 +1,268 @@
+// Medusa head projections over many rows (the verify-pass shape: every tree
+// node of every sequence, M = B*T rows; also the backbone's LM head, a head
+// with W1 = 0, over the same rows).  Same arithmetic as the skinny kernels in
+// heads.hip (bf16 products, fp32 accumulation, the same fused epilogues), but
+// at M in the hundreds to ten-thousands the weights are re-used M times and
+// the work is matrix-core bound, so the kernel is a classic block-tiled GEMM:
+//
+//   out[head][m][n] = sum_i W[head][n][i] * X[head][m][i]
+//
+// Block tile BN (weight rows n) x BM (activation rows m), reduction tile 64.
+// Both operand tiles go global -> registers -> LDS: two LDS stages and two
+// register sets, so while one stage feeds the MFMAs the next tile waits in
+// registers and the one after is being loaded; one barrier per reduction
+// tile.  LDS rows are padded to 144 bytes.  Eight waves per block, each owning a TN x TM sub-tile of
+// v_mfma_f32_16x16x32_bf16 accumulators with the weight tile as the A operand,
+// so D[n][m] lands as four consecutive n of one m per lane: one 16-byte fp32
+// store (logits) or one 8-byte bf16 store (ResBlock) per fragment.
+//
+// Block order: consecutive block ids are dealt round-robin to the 8 XCDs, so
+// ids are remapped to make each XCD run a contiguous range of tiles, and the
+// range is ordered in groups of GM activation tiles (m fastest), so the blocks
+// that run together on one XCD share both weight and activation tiles in its
+// L2.
+#include "common.h"
+#include "gemm.h"
+
+using namespace medusa;
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kBK = 64;          // reduction tile (two MFMA k-steps)
+constexpr int kLdk = kBK + 8;    // padded LDS row, elements (144 bytes)
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int BN, int BM, int WGN, int WGM>
+struct TileShape {
+  static constexpr int kThreads = 64 * WGN * WGM;
+  static constexpr int TN = BN / WGN, TM = BM / WGM;   // wave sub-tile
+  static constexpr int FN = TN / 16, FM = TM / 16;     // MFMA tiles per wave
+  static constexpr int WCH = BN * 8 / kThreads;        // 16-byte chunks per thread per k-tile
+  static constexpr int XCH = BM * 8 / kThreads;
+  static constexpr int kStage = (BN + BM) * kLdk;      // elements per LDS stage
+  static constexpr size_t kLdsBytes = 2 * kStage * sizeof(uint16_t);
+  static_assert(TN % 16 == 0 && TM % 16 == 0, "wave tile");
+  static_assert((BN * 8) % kThreads == 0 && (BM * 8) % kThreads == 0, "load split");
+  static_assert(BN % 16 == 0, "packed tiles");
+};
+
+template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM>
+__global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
+    const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
+    int H, int M, int GM, const uint16_t *__restrict__ resid, uint16_t *__restrict__ out_bf16,
+    float *__restrict__ out_f32) {
+  using S = TileShape<BN, BM, WGN, WGM>;
+  extern __shared__ u32x4_t lds_raw[];
+  uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
+
+  // ---- tile of this block
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  const int per_head = tiles_n * tiles_m;
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = id / per_head;
+  id -= head * per_head;
+  const int span = GM * tiles_n;
+  const int grp = id / span;
+  const int mfirst = grp * GM;
+  const int gm = min(GM, tiles_m - mfirst);
+  const int rem = id - grp * span;
+  const int m0 = (mfirst + rem % gm) * BM, n0 = (rem / gm) * BN;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wn = wave % WGN, wm = wave / WGN;
+
+  // ---- per-thread load slots: 32-bit byte offsets from the head's base (the
+  // launcher checks that a head's operands span less than 4 GiB; rows past the
+  // end re-read the last row) and LDS destinations, affine in the slot j.
+  const int NTt = (N + 15) / 16, Ssteps = H / 32;
+  const char *wbase = reinterpret_cast<const char *>(W) + (PACKED ? (size_t)head * NTt * Ssteps * 1024
+                                                                   : (size_t)head * N * H * 2);
+  const char *xbase = reinterpret_cast<const char *>(X) + (size_t)head * x_head_stride * 2;
+  uint32_t woff[S::WCH], xoff[S::XCH];
+#pragma unroll
+  for (int j = 0; j < S::WCH; ++j) {
+    const int c = tid + j * S::kThreads;
+    if (PACKED) {
+      // slot c: lane c%64 of fragment (row tile c/128, k-step (c/64)%2)
+      const int t = min(n0 / 16 + (c >> 7), NTt - 1);
+      woff[j] = ((uint32_t)(t * Ssteps + ((c >> 6) & 1)) * 64u + (uint32_t)(c & 63)) * 16u;
+    } else {
+      // slot c: row c/8, columns 8*(c%8)..+7 (each row's 128 bytes in 8 lanes)
+      const int n = min(n0 + (c >> 3), N - 1);
+      woff[j] = ((uint32_t)n * (uint32_t)H + (uint32_t)(c & 7) * 8u) * 2u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < S::XCH; ++j) {
+    const int c = tid + j * S::kThreads;
+    const int m = min(m0 + (c >> 3), M - 1);
+    xoff[j] = ((uint32_t)m * (uint32_t)H + (uint32_t)(c & 7) * 8u) * 2u;
+  }
+  // LDS destinations (elements): packed slot -> row 16*(c/128) + l%16, column
+  // 32*((c/64)%2) + 8*(l/16) with l = c%64; row-major slot -> row c/8, column 8*(c%8)
+  constexpr int kWdstStep = PACKED ? (S::kThreads / 128) * 16 * kLdk : (S::kThreads / 8) * kLdk;
+  const int wdst0 = PACKED ? ((tid >> 7) * 16 + (tid & 15)) * kLdk + ((tid >> 6) & 1) * 32 + ((tid >> 4) & 3) * 8
+                           : (tid >> 3) * kLdk + (tid & 7) * 8;
+  const int xdst0 = BN * kLdk + (tid >> 3) * kLdk + (tid & 7) * 8;
+  constexpr int kXdstStep = (S::kThreads / 8) * kLdk;
+  const uint32_t w_step = PACKED ? 2u * 1024u : kBK * 2u;   // bytes per k-tile
+
+  // two register sets: tile j is loaded into set j % 2
+  u32x4_t wreg[2][S::WCH], xreg[2][S::XCH];
+  auto load = [&](int kt, int set) {
+    const uint32_t wk = (uint32_t)kt * w_step, xk = (uint32_t)kt * (kBK * 2u);
+#pragma unroll
+    for (int j = 0; j < S::WCH; ++j) wreg[set][j] = *reinterpret_cast<const u32x4_t *>(wbase + (woff[j] + wk));
+#pragma unroll
+    for (int j = 0; j < S::XCH; ++j) xreg[set][j] = *reinterpret_cast<const u32x4_t *>(xbase + (xoff[j] + xk));
+  };
+  auto stash = [&](int set, int stage) {
+    uint16_t *base = lds + stage * S::kStage;
+#pragma unroll
+    for (int j = 0; j < S::WCH; ++j) *reinterpret_cast<u32x4_t *>(base + wdst0 + j * kWdstStep) = wreg[set][j];
+#pragma unroll
+    for (int j = 0; j < S::XCH; ++j) *reinterpret_cast<u32x4_t *>(base + xdst0 + j * kXdstStep) = xreg[set][j];
+  };
+
+  f32x4_t acc[S::FN][S::FM];
+#pragma unroll
+  for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+    for (int g = 0; g < S::FM; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // fragment read offsets within a stage (row lr of the tile, k slice 8*lg)
+  const int a_off = (wn * S::TN + lr) * kLdk + lg * 8;
+  const int b_off = BN * kLdk + (wm * S::TM + lr) * kLdk + lg * 8;
+  auto compute = [&](int stage) {
+    const uint16_t *base = lds + stage * S::kStage;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      u32x4_t a[S::FN], b[S::FM];
+#pragma unroll
+      for (int f = 0; f < S::FN; ++f) a[f] = *reinterpret_cast<const u32x4_t *>(base + a_off + f * 16 * kLdk + ks * 32);
+#pragma unroll
+      for (int g = 0; g < S::FM; ++g) b[g] = *reinterpret_cast<const u32x4_t *>(base + b_off + g * 16 * kLdk + ks * 32);
+#pragma unroll
+      for (int f = 0; f < S::FN; ++f)
+#pragma unroll
+        for (int g = 0; g < S::FM; ++g) acc[f][g] = mfma(a[f], b[g], acc[f][g]);
+    }
+  };
+
+  // Software pipeline, two k-tiles per trip (H % 128 == 0, so nk is even):
+  // while stage s feeds the MFMAs, tile kt+1 waits in registers (loaded one
+  // compute phase earlier) and tile kt+2 is being loaded, so every global
+  // load has two compute phases to arrive.  Loads past the end re-read the
+  // last tile into a stage that is never read again, keeping the trip
+  // branch-free.
+  const int nk = H / kBK;
+  load(0, 0);
+  load(min(1, nk - 1), 1);
+  stash(0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    load(min(kt + 2, nk - 1), 0);
+    compute(0);
+    stash(1, 1);
+    __syncthreads();
+    load(min(kt + 3, nk - 1), 1);
+    compute(1);
+    stash(0, 0);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[n + v][m], v < 4, for n = tile + 4*lg, m = tile + lr
+  const bool vec = (N % 4) == 0;
+#pragma unroll
+  for (int g = 0; g < S::FM; ++g) {
+    const int m = m0 + wm * S::TM + g * 16 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f) {
+      const int n = n0 + wn * S::TN + f * 16 + lg * 4;
+      if (n >= N) continue;
+      const f32x4_t v = acc[f][g];
+      const size_t o = ((size_t)head * M + m) * N + n;
+      if (EPI == kEpiLogits) {
+        if (vec) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(out_f32 + o));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) out_f32[o + e] = v[e];
+        }
+      } else {
+        // N == H here; H % 128 == 0 so the four columns are in range and aligned
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t *>(resid + (size_t)m * H + n);
+        uint16_t hb[4] = {(uint16_t)(hv[0] & 0xffffu), (uint16_t)(hv[0] >> 16), (uint16_t)(hv[1] & 0xffffu),
+                          (uint16_t)(hv[1] >> 16)};
+        uint16_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float u = v[e];
+          r[e] = f32_to_bf16_rne(bf16_to_f32(hb[e]) + u / (1.0f + expf(-u)));
+        }
+        const u32x2_t rv = {(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+        *reinterpret_cast<u32x2_t *>(out_bf16 + o) = rv;
+      }
+    }
+  }
+}
+
+template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM>
+medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N,
+                           int H, int M, int GM, const uint16_t *resid, uint16_t *ob, float *of) {
+  using S = TileShape<BN, BM, WGN, WGM>;
+  auto kern = head_gemm_tiled<EPI, PACKED, BN, BM, WGN, WGM>;
+  static bool attr_set = false;   // per instantiation; setting it twice is harmless
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)S::kLdsBytes) != hipSuccess)
+      return fail(MEDUSA_ERR_HIP, "head projection: cannot reserve %zu bytes of LDS", S::kLdsBytes);
+    attr_set = true;
+  }
+  const long blocks = (long)K * ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
+  if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(S::kThreads), S::kLdsBytes, st, W, X, xhs, N, H, M,
+                     GM, resid, ob, of);
+  return check_launch(EPI == kEpiLogits ? "medusa_head_vocab (tiled)" : "medusa_head_resblock (tiled)");
+}
+
+}  // namespace
+
+namespace medusa {
+
+template <int EPI, bool PACKED>
+medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
+                                  int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
+  if (H % kBK != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% %d != 0 (H=%d)", kBK, H);
+  const size_t w_head = PACKED ? (size_t)((N + 15) / 16) * (H / 32) * 1024 : (size_t)N * H * 2;
+  if (w_head >= (1ull << 32) || (size_t)M * H * 2 >= (1ull << 32))
+    return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
+  return launch_tiled<EPI, PACKED, 256, 256, 2, 4>(st, W, X, xhs, K, N, H, M, 8, resid, ob, of);
+}
+
+template medusa_status head_gemm_many_rows<kEpiResblock, false>(hipStream_t, const uint16_t *, const uint16_t *,
+                                                                long, int, int, int, int, const uint16_t *,
+                                                                uint16_t *, float *);
+template medusa_status head_gemm_many_rows<kEpiResblock, true>(hipStream_t, const uint16_t *, const uint16_t *,
+                                                               long, int, int, int, int, const uint16_t *,
+                                                               uint16_t *, float *);
+template medusa_status head_gemm_many_rows<kEpiLogits, false>(hipStream_t, const uint16_t *, const uint16_t *,
+                                                              long, int, int, int, int, const uint16_t *,
+                                                              uint16_t *, float *);
+template medusa_status head_gemm_many_rows<kEpiLogits, true>(hipStream_t, const uint16_t *, const uint16_t *,
+                                                             long, int, int, int, int, const uint16_t *,
+                                                             uint16_t *, float *);
+
+}  // namespace medusa

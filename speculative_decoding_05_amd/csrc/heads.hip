@@ -2,6 +2,7 @@
 //
 // At decode time the heads see one row per sequence (M <= 32), so both
 // projections are skinny GEMMs whose cost is streaming W1 / W2 from HBM once.
+// More rows (the verify-pass shape) go to the block-tiled kernel in gemm.hip.
 // bf16 path: each wave owns 16*R output rows and a quarter of the reduction;
 // the weight slab is the MFMA A operand (v_mfma_f32_16x16x32_bf16: lane l
 // holds row l%16, reduction slice 8*(l/16)..+7), activations are the B operand
@@ -16,6 +17,7 @@
 // rate that the row-major pattern loses to scattered row segments.  Weights are
 // read with non-temporal loads so the small activation block stays in L2.
 #include "common.h"
+#include "gemm.h"
 
 using namespace medusa;
 
@@ -28,7 +30,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-enum { EPI_RESBLOCK = 0, EPI_LOGITS = 1 };
+constexpr int EPI_RESBLOCK = kEpiResblock, EPI_LOGITS = kEpiLogits;
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -239,24 +241,21 @@ void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, 
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  for (int m0 = 0; m0 < M; m0 += MEDUSA_MAX_HEADS_M) {
-    const int Mg = M - m0 < MEDUSA_MAX_HEADS_M ? M - m0 : MEDUSA_MAX_HEADS_M;
-    if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
-      launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
-      launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
-      launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    else if (Mg <= 4)
-      launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    else if (Mg <= 16)
-      launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    else
-      launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
-    medusa_status s = check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
-    if (s != MEDUSA_OK) return s;
-  }
-  return MEDUSA_OK;
+  if (M >= kManyRows) return head_gemm_many_rows<EPI, PACKED>(st, W, X, xhs, K, N, H, M, resid, ob, of);
+  const int m0 = 0, Mg = M;   // one group: the weights are streamed once
+  if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
+    launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
+    launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
+    launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (Mg <= 4)
+    launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (Mg <= 16)
+    launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else
+    launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
 }
 
 template <int EPI>

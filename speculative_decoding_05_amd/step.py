@@ -116,6 +116,39 @@ class Step:
         self.accept(i)
 
 
+class VerifyPass:
+    """The verify pass's dense contractions over all M = B*T tree nodes (bf16):
+    the Medusa heads on every node's hidden state, and the backbone's LM head
+    (a head with W1 = 0) turning the tree-attention output of `step` into
+    verification logits.  Inputs are seeded device-side normals."""
+
+    def __init__(self, step: Step, seed: int = 0):
+        cfg, T = step.cfg, step.tree.T
+        if not step.packed:
+            raise ValueError("the verify pass runs on the bf16 (packed-weight) path")
+        self.step, self.M = step, cfg.B * T
+        M, H, V, K = self.M, cfg.H, cfg.V, cfg.K
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        self.h = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+        W_lm = (torch.randn((1, V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        self.W_lm = mb.PackedWeights(W_lm)
+        torch.cuda.synchronize()
+        del W_lm
+        self.r = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")
+        self.logits = torch.empty((K, M, V), dtype=torch.float32, device="cuda")
+        self.vlogits = torch.empty((1, M, V), dtype=torch.float32, device="cuda")
+
+    def heads_resblock(self):
+        mb.medusa_head_resblock_packed(self.h, self.step.W1p, self.r)
+
+    def heads_vocab(self):
+        mb.medusa_head_vocab_packed(self.r, self.step.W2p, self.logits)
+
+    def lm_head(self):
+        c = self.step.cfg
+        mb.medusa_head_vocab_packed(self.step.attn.reshape(1, self.M, c.H), self.W_lm, self.vlogits)
+
+
 def host_inputs(cfg: configs.Config, T: int, B: int | None = None, L: int | None = None) -> dict:
     """All seeded inputs of a configuration except the verification logits."""
     W1, W2 = synth.head_weights(cfg)

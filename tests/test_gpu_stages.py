@@ -43,8 +43,11 @@ def run_heads(dtype, h, W1, W2, packed=False):
     ("bf16", 2, 5, 384, 520),
     ("bf16", 2, 16, 256, 64),
     ("bf16", 2, 17, 256, 300),      # two column tiles
-    ("bf16", 1, 40, 128, 96),       # two row groups of the launch
     ("bf16", 4, 3, 1024, 2048),     # the unrolled k loop
+    # many rows: the block-tiled kernel (verify-pass shape)
+    ("bf16", 1, 33, 128, 96),       # first row count past the streaming kernel
+    ("bf16", 2, 300, 512, 1001),    # ragged row tile, V % 4 != 0 (scalar stores)
+    ("bf16", 1, 520, 384, 264),     # three row tiles x two column tiles, 6 k-tiles
     ("f32", 2, 1, 256, 1000),       # the tiny fp32 configuration
     ("f32", 3, 9, 64, 130),
 ])
@@ -81,9 +84,25 @@ def test_zero_w1_reproduces_lm_head_bitwise(dtype):
     assert rel_err(lg_g[0], ref) <= TOL[dtype]
 
 
+def test_zero_w1_many_rows_bitwise():
+    # the tiled kernel: W1 = 0 => r = h exactly, and the LM head over all rows
+    # (medusa_head_vocab with one head) equals every head's projection
+    K, M, H, V = 2, 100, 256, 700
+    h, _, W2 = head_inputs("bf16", 1, M, H, V, seed=17)
+    W1 = np.zeros((K, H, H), dtype=h.dtype)
+    r_g, lg_g = run_heads("bf16", h, W1, np.concatenate([W2] * K), packed=True)
+    assert np.array_equal(r_g, np.stack([synth.as_f64(h)] * K))
+    assert np.array_equal(lg_g[1], lg_g[0])
+    logits = torch.empty((1, M, V), dtype=torch.float32, device="cuda")
+    mb.medusa_head_vocab_packed(dev(h).reshape(1, M, H).contiguous(), mb.PackedWeights(dev(W2)), logits)
+    assert np.array_equal(host(logits)[0], lg_g[0])
+    ref = oracle.verification_logits(synth.as_f64(h)[None], synth.as_f64(W2[0]))[0]
+    assert rel_err(lg_g[0], ref) <= TOL["bf16"]
+
+
 def test_packed_equals_row_major_bitwise():
     # the packed layout only changes where the weights sit, not the arithmetic
-    for K, M, H, V in [(4, 1, 512, 1000), (2, 20, 256, 333)]:
+    for K, M, H, V in [(4, 1, 512, 1000), (2, 20, 256, 333), (2, 300, 256, 1001)]:
         h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=M)
         a = run_heads("bf16", h, W1, W2, packed=False)
         b = run_heads("bf16", h, W1, W2, packed=True)
@@ -102,8 +121,9 @@ def test_pack_layout():
         assert Wp[k, t, s_, l].tolist() == np.asarray(want, np.int64).tolist()
 
 
-def test_heads_rows_and_heads_independent_bitwise():
-    K, M, H, V = 3, 6, 256, 300
+@pytest.mark.parametrize("M", [6, 70])
+def test_heads_rows_and_heads_independent_bitwise(M):
+    K, H, V = 3, 256, 300
     h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=9)
     _, a = run_heads("bf16", h, W1, W2)
     perm = rng(1).permutation(M)
@@ -400,3 +420,29 @@ def test_whole_step_is_deterministic():
                                                s.best, s.next_tok, s.accepted)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ verify pass
+def test_verify_pass_lm_head_on_attention_output():
+    # the backbone's LM head over every tree node (M = B*T rows, the tiled
+    # kernel) turning the attention output into verification logits
+    paths = oracle.greedy_paths(configs.acc_exact, 4, 63, 10)
+    ot = oracle.build_tree(paths, 4, 10)
+    t = mb.Tree(paths, 4, 10).upload()
+    B, nh, dh, L, V = 3, 4, 64, 150, 1500
+    H = nh * dh
+    g = rng(41)
+    mk = lambda shape, s=1.0: store((g.standard_normal(shape) * s).astype(np.float32), "bf16")
+    q, kt, vt = mk((B, t.T, nh, dh)), mk((B, t.T, nh, dh)), mk((B, t.T, nh, dh))
+    kc, vc = mk((B, nh, L, dh)), mk((B, nh, L, dh))
+    W_lm = mk((V, H), 0.05)
+    o = torch.empty((B, t.T, nh, dh), dtype=torch.bfloat16, device="cuda")
+    mb.tree_attention(t, dev(q), dev(kt), dev(vt), dev(kc), dev(vc), o)
+    z = torch.empty((1, B * t.T, V), dtype=torch.float32, device="cuda")
+    mb.medusa_head_vocab_packed(o.reshape(1, B * t.T, H), mb.PackedWeights(dev(W_lm)[None].contiguous()), z)
+    f = synth.as_f64
+    o_ref = oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot)
+    z_ref = oracle.verification_logits(o_ref.reshape(B, t.T, H), f(W_lm))
+    got = host(z)[0].reshape(B, t.T, V)
+    for b in range(B):
+        assert rel_err(got[b], z_ref[b]) <= TOL["bf16"], b

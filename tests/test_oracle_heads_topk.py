@@ -26,6 +26,23 @@ def test_zero_w1_reproduces_lm_head_exactly():
             assert np.array_equal(out[k], ref)
 
 
+def test_verification_logits_brute_force_and_zero_w1_head():
+    # small integers: every product and sum is exact in float64, so explicit
+    # loops give the exact answer
+    g = np.random.default_rng(3)
+    B, T, H, V = 2, 3, 5, 7
+    x = g.integers(-4, 5, (B, T, H)).astype(np.float64)
+    W = g.integers(-3, 4, (V, H)).astype(np.float64)
+    z = oracle.verification_logits(x, W)
+    for b in range(B):
+        for t in range(T):
+            for v in range(V):
+                assert z[b, t, v] == sum(W[v, i] * x[b, t, i] for i in range(H))
+    # and it is the W1 = 0 head: the LM head the heads start from
+    head = oracle.medusa_heads(x.reshape(B * T, H), np.zeros((1, H, H)), W[None])[0]
+    assert np.array_equal(z.reshape(B * T, V), head)
+
+
 def test_silu_residual_closed_form():
     g = np.random.default_rng(1)
     M, H = 4, 16
