@@ -14,6 +14,7 @@
  *       medusa_tree_tokens  the token of every tree node
  *   (3) tree_attention      every node over the prefix KV cache + its ancestors
  *   (4) typical_accept      typical acceptance and the longest accepted prefix
+ *   (5) medusa_kv_commit    append the accepted path to the KV cache
  *
  * Conventions (all calls):
  *  - Device buffers are plain device pointers owned by the caller; tensors are
@@ -224,6 +225,17 @@ medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medu
                              const void *k_tree, const void *v_tree, const void *k_cache,
                              const void *v_cache, void *out, void *ws, size_t ws_bytes);
 
+/* Ragged prefixes (decode loop): the cache is [B][nh][L_cap][dh] and sequence
+ * b attends to its first seq_len[b] cached keys (device int32 [B]; values
+ * are clamped to [0, L_max]).  L_max <= L_cap is the host's bound on the
+ * lengths and sizes the launch; ws: tree_attention_workspace(dt, t, B, nh,
+ * dh, L_max) bytes.  Otherwise as tree_attention. */
+medusa_status tree_attention_ragged(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                                    int B, int nh, int dh, int L_cap, int L_max,
+                                    const int32_t *seq_len, float scale, const void *q,
+                                    const void *k_tree, const void *v_tree, const void *k_cache,
+                                    const void *v_cache, void *out, void *ws, size_t ws_bytes);
+
 /* ------------------------------------------------------------------------- */
 /* (4) Typical acceptance.  Paper summary, "基准/方法设计" (third component) and
  *     "方法细节" (temperature): candidate token x at node c is kept if
@@ -250,6 +262,28 @@ medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B
                              float delta, float temperature, int32_t *accept_len,
                              int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
                              float *cand_p, float *row_thr, void *ws, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------- */
+/* (5) KV-cache commit.  Paper summary, "基准/方法设计" (the accepted prefix
+ *     is kept and the next round starts after it) and tutorial page
+ *     "部署与生成" (generation keeps the key/value cache): the K/V rows of
+ *     the accepted path root..best_node[b] -- depth(best)+1 rows, in depth
+ *     order -- are appended to sequence b's cache at positions
+ *     seq_len[b] + depth (each node's tree position), then seq_len[b] grows
+ *     by the rows written and, if next_tok / root_tok are given,
+ *     root_tok[b] = next_tok[b] (the next step's root).
+ *  k_tree, v_tree   [B][T][nh][dh]      device, dt
+ *  best_node        [B]                 device int32 (typical_accept output)
+ *  seq_len          [B]                 device int32, in/out
+ *  k_cache, v_cache [B][nh][L_cap][dh]  device, dt, updated in place
+ *  next_tok, root_tok [B]               device int32, both or neither (NULL)
+ *  Rows that would pass L_cap are dropped (seq_len stops at L_cap); a
+ *  sequence with best_node outside [0, T) or seq_len outside [0, L_cap] is
+ *  left unchanged (its root is still advanced).  Needs dh * elem % 16 == 0. */
+medusa_status medusa_kv_commit(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t, int B,
+                               int nh, int dh, int L_cap, const void *k_tree, const void *v_tree,
+                               const int32_t *best_node, int32_t *seq_len, void *k_cache,
+                               void *v_cache, const int32_t *next_tok, int32_t *root_tok);
 
 #ifdef __cplusplus
 }

@@ -430,6 +430,46 @@ def typical_accept(logits, tree_tok, tree, eps, delta, temperature=1.0):
 
 
 # ----------------------------------------------------------------------------
+# (5) KV-cache commit -- [P3] "基准/方法设计" (the next round starts after the
+#     accepted prefix), [P2] "部署与生成" (generation keeps the KV cache)
+# ----------------------------------------------------------------------------
+def kv_commit(tree, k_tree, v_tree, best, seq_len, k_cache, v_cache):
+    """Append each sequence's accepted path to its prefix cache.
+
+    The accepted tokens are the path root..best; keeping their keys and values
+    lets the next step treat them as ordinary prefix tokens.  Reading: node j
+    of the path is written at its tree position seq_len[b] + depth(j)
+    (tree_positions), so the cache holds prefix, root, ..., best in order;
+    rows that would pass the cache capacity L_cap are dropped; a sequence
+    whose best is not a node, or whose length is outside [0, L_cap], is left
+    unchanged.
+    k_tree, v_tree [B][T][nh][dh]; k_cache, v_cache [B][nh][L_cap][dh];
+    best, seq_len [B].  Returns new (k_cache, v_cache, seq_len) (copies).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    lens = np.array(seq_len, dtype=np.int64, copy=True)
+    B, T = k_tree.shape[0], k_tree.shape[1]
+    L_cap = kc.shape[2]
+    for b in range(B):
+        j, L = int(best[b]), int(lens[b])
+        if not (0 <= j < T and 0 <= L <= L_cap):
+            continue
+        pos = tree_positions(tree, L)
+        path = ancestors(tree, j)             # root .. j, increasing depth
+        n = 0
+        for node in path:
+            p = int(pos[node])
+            if p >= L_cap:
+                break
+            kc[b, :, p] = k_tree[b, node]
+            vc[b, :, p] = v_tree[b, node]
+            n += 1
+        lens[b] = L + n
+    return kc, vc, lens
+
+
+# ----------------------------------------------------------------------------
 # the whole step
 # ----------------------------------------------------------------------------
 def topk_per_head(logits, k):

@@ -57,6 +57,8 @@ SIGNATURES = {
     "medusa_topk_tree_tokens": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz]),
     "tree_attention_workspace": (_sz, [_i, _p, _i, _i, _i, _i]),
     "tree_attention": (_i, [_p, _i, _p, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "tree_attention_ragged": (_i, [_p, _i, _p, _i, _i, _i, _i, _i, _p, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "medusa_kv_commit": (_i, [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "typical_accept_workspace": (_sz, [_p, _i, _i]),
     "typical_accept": (_i, [_p, _p, _i, _i, _p, _p, _f, _f, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
 }
@@ -307,6 +309,31 @@ def tree_attention(tree, q, k_tree, v_tree, k_cache, v_cache, out, scale=0.0, ws
 
 
 # ---------------------------------------------------------------- acceptance
+def tree_attention_ragged(tree, q, k_tree, v_tree, k_cache, v_cache, seq_len, L_max, out, scale=0.0, ws=None):
+    """As tree_attention with a cache of capacity L_cap = k_cache.shape[2] and
+    per-sequence prefix lengths seq_len [B] (device int32, each <= L_max)."""
+    _dev(q, k_tree, v_tree, k_cache, v_cache, seq_len, out, ws)
+    B, T, nh, dh = q.shape
+    L_cap = k_cache.shape[2]
+    dt = _dtype_code(q)
+    if ws is None:
+        ws = workspace(tree_attention_workspace(dt, tree, B, nh, dh, L_max), q.device)
+    check(lib.tree_attention_ragged(_stream(), dt, tree.handle, B, nh, dh, L_cap, L_max, _ptr(seq_len),
+                                    float(scale), _ptr(q), _ptr(k_tree), _ptr(v_tree), _ptr(k_cache),
+                                    _ptr(v_cache), _ptr(out), _ptr(ws), ws.numel()))
+    return out
+
+
+def kv_commit(tree, k_tree, v_tree, best_node, seq_len, k_cache, v_cache, next_tok=None, root_tok=None):
+    """Append each sequence's accepted path (root..best_node) to its cache
+    [B][nh][L_cap][dh] at seq_len; seq_len grows in place; root_tok <- next_tok."""
+    _dev(k_tree, v_tree, best_node, seq_len, k_cache, v_cache, next_tok, root_tok)
+    B, T, nh, dh = k_tree.shape
+    check(lib.medusa_kv_commit(_stream(), _dtype_code(k_tree), tree.handle, B, nh, dh, k_cache.shape[2],
+                               _ptr(k_tree), _ptr(v_tree), _ptr(best_node), _ptr(seq_len), _ptr(k_cache),
+                               _ptr(v_cache), _ptr(next_tok), _ptr(root_tok)))
+
+
 def typical_accept_workspace(tree, B, V):
     return lib.typical_accept_workspace(tree.handle, B, V)
 

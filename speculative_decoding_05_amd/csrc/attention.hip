@@ -133,8 +133,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)
 // STAGES tiles are prefetched into registers ahead of the one being consumed.
 template <int DH, int QT, int STAGES>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
-    int B, int nh, int T, int W, int L, float scale_log2, int qgroups, int nsplit, int per_split,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
+    int B, int nh, int T, int W, int L, int Lstride, const int32_t *__restrict__ seq_len, float scale_log2,
+    int qgroups, int nsplit, int per_split, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const uint64_t *__restrict__ mask,
     uint16_t *__restrict__ out, float *__restrict__ ws_o, float2 *__restrict__ ws_ml) {
   constexpr int DS = DH / 32;  // 32-wide reduction steps over the head dim
@@ -171,9 +171,11 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
       qreg[qt][s] = qvalid[qt] ? *reinterpret_cast<const u32x4_t *>(qp + s * 32) : u32x4_t{0u, 0u, 0u, 0u};
   }
 
-  // key ranges: prefix slice [c0, c1), then (last slice only) the T tree keys
+  // key ranges: prefix slice [c0, c1) of this sequence's Lb cached keys, then
+  // (last slice only) the T tree keys
+  const int Lb = seq_len ? min(max(seq_len[b], 0), L) : L;
   const int c0 = split * per_split;
-  const int c1 = min(L, c0 + per_split);
+  const int c1 = min(Lb, c0 + per_split);
   const int ncache = c1 > c0 ? (c1 - c0 + kKT - 1) / kKT : 0;
   const bool last = split == nsplit - 1;
   const int ntree = last ? (T + kKT - 1) / kKT : 0;
@@ -181,8 +183,8 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
 
   const long cache_stride = DH;
   const long tree_stride = (long)nh * DH;
-  const uint16_t *kc_bh = kc + ((size_t)b * nh + h) * L * DH;
-  const uint16_t *vc_bh = vc + ((size_t)b * nh + h) * L * DH;
+  const uint16_t *kc_bh = kc + ((size_t)b * nh + h) * Lstride * DH;
+  const uint16_t *vc_bh = vc + ((size_t)b * nh + h) * Lstride * DH;
   const uint16_t *kt_bh = kt + ((size_t)b * T * nh + h) * DH;
   const uint16_t *vt_bh = vt + ((size_t)b * T * nh + h) * DH;
 
@@ -393,7 +395,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T
 // fp32 path: block = (b, h, 32 queries); keys = lanes; K/V tiles in LDS.
 constexpr int kF32Q = 32;
 template <int DH>
-__global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W, int L, float scale,
+__global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W, int L, int Lstride,
+                                                     const int32_t *__restrict__ seq_len, float scale,
                                                      int qgroups, const float *__restrict__ q,
                                                      const float *__restrict__ kt,
                                                      const float *__restrict__ vt,
@@ -421,19 +424,20 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
 #pragma unroll
     for (int j = 0; j < DPL; ++j) o[u][j] = 0.f;
   }
-  const int ncache = (L + kKT - 1) / kKT;
+  const int Lb = seq_len ? min(max(seq_len[b], 0), L) : L;
+  const int ncache = (Lb + kKT - 1) / kKT;
   const int ntiles = ncache + (T + kKT - 1) / kKT;
   for (int tile = 0; tile < ntiles; ++tile) {
     const bool is_tree = tile >= ncache;
     const int r0 = is_tree ? (tile - ncache) * kKT : tile * kKT;
-    const int rend = is_tree ? T : L;
+    const int rend = is_tree ? T : Lb;
     __syncthreads();
     for (int e = threadIdx.x; e < kKT * DH; e += 256) {
       const int r = e / DH, d = e % DH, row = r0 + r;
       float kv = 0.f, vv = 0.f;
       if (row < rend) {
         const size_t off = is_tree ? (((size_t)b * T + row) * nh + h) * DH + d
-                                   : (((size_t)b * nh + h) * L + row) * DH + d;
+                                   : (((size_t)b * nh + h) * Lstride + row) * DH + d;
         kv = is_tree ? kt[off] : kc[off];
         vv = is_tree ? vt[off] : vc[off];
       }
@@ -480,10 +484,18 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
   }
 }
 
+// Cache layout [B][nh][Lstride][dh]; sequence b attends to its first
+// seq_len[b] cached keys (all L when seq_len is NULL), clamped to [0, L].
+struct Prefix {
+  int L, Lstride;
+  const int32_t *seq_len;
+};
+
 template <int DH, int QT>
-medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, int L, float scale,
+medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, float scale,
                           const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                           const void *v_cache, void *out, void *ws) {
+  const int L = pf.L;
   const Split sp = choose_split(B, nh, t->T, L);
   const int qgroups = (t->T + kQB * QT - 1) / (kQB * QT);
   const long nblocks = (long)B * nh * qgroups * sp.nsplit;
@@ -495,7 +507,7 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, i
     ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
   }
   hipLaunchKernelGGL((tree_attn_bf16<DH, QT, QT == 1 ? 2 : 1>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
-                     t->W, L, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
+                     t->W, L, pf.Lstride, pf.seq_len, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
                      static_cast<const uint16_t *>(v_cache), t->d_mask, static_cast<uint16_t *>(out),
@@ -510,12 +522,12 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, i
 }
 
 template <int DH>
-medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, int L, float scale,
+medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, float scale,
                          const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                          const void *v_cache, void *out) {
   const int qgroups = (t->T + kF32Q - 1) / kF32Q;
-  hipLaunchKernelGGL((tree_attn_f32<DH>), dim3(B * nh * qgroups), dim3(256), 0, st, B, nh, t->T, t->W, L,
-                     scale, qgroups, static_cast<const float *>(q), static_cast<const float *>(k_tree),
+  hipLaunchKernelGGL((tree_attn_f32<DH>), dim3(B * nh * qgroups), dim3(256), 0, st, B, nh, t->T, t->W, pf.L,
+                     pf.Lstride, pf.seq_len, scale, qgroups, static_cast<const float *>(q), static_cast<const float *>(k_tree),
                      static_cast<const float *>(v_tree), static_cast<const float *>(k_cache),
                      static_cast<const float *>(v_cache), t->d_mask, static_cast<float *>(out));
   return check_launch("tree_attention");
@@ -531,35 +543,60 @@ extern "C" size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t
   return (size_t)sp.nsplit * B * nh * t->T * (dh + 2) * sizeof(float);
 }
 
-extern "C" medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
-                                        int B, int nh, int dh, int L, float scale, const void *q,
-                                        const void *k_tree, const void *v_tree, const void *k_cache,
-                                        const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+namespace {
+
+medusa_status attention_entry(const char *who, medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                              int B, int nh, int dh, Prefix pf, float scale, const void *q, const void *k_tree,
+                              const void *v_tree, const void *k_cache, const void *v_cache, void *out, void *ws,
+                              size_t ws_bytes) {
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
-  if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return fail(MEDUSA_ERR_ARG, "tree_attention: unknown dtype");
-  if (B < 1 || nh < 1 || L < 0) return fail(MEDUSA_ERR_ARG, "tree_attention: B=%d nh=%d L=%d", B, nh, L);
-  if (dh != 64 && dh != 128) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: dh=%d not in {64, 128}", dh);
-  if (!(scale >= 0.f) || !isfinite(scale)) return fail(MEDUSA_ERR_ARG, "tree_attention: bad scale");
+  const int L = pf.L;
+  if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return fail(MEDUSA_ERR_ARG, "%s: unknown dtype", who);
+  if (B < 1 || nh < 1 || L < 0 || pf.Lstride < L)
+    return fail(MEDUSA_ERR_ARG, "%s: B=%d nh=%d L=%d stride=%d", who, B, nh, L, pf.Lstride);
+  if (dh != 64 && dh != 128) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: dh=%d not in {64, 128}", who, dh);
+  if (!(scale >= 0.f) || !isfinite(scale)) return fail(MEDUSA_ERR_ARG, "%s: bad scale", who);
   if (!q || !k_tree || !v_tree || !out || (L > 0 && (!k_cache || !v_cache)))
-    return fail(MEDUSA_ERR_ARG, "tree_attention: NULL pointer");
+    return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
   if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
       (L > 0 && (!aligned16(k_cache) || !aligned16(v_cache))))
-    return fail(MEDUSA_ERR_ARG, "tree_attention: pointers must be 16-byte aligned");
+    return fail(MEDUSA_ERR_ARG, "%s: pointers must be 16-byte aligned", who);
   const size_t need = tree_attention_workspace(dt, t, B, nh, dh, L);
   if (ws_bytes < need || (need > 0 && !ws))
-    return fail(MEDUSA_ERR_WORKSPACE, "tree_attention: workspace %zu < %zu", ws_bytes, need);
-  if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "tree_attention: workspace must be 16-byte aligned");
+    return fail(MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, need);
+  if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)dh) : scale;
   hipStream_t st = as_stream(stream);
   if (dt == MEDUSA_BF16) {
     const bool two = qtiles_for(t->T) == 2;
     if (dh == 128)
-      return two ? launch_bf16<128, 2>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
-                 : launch_bf16<128, 1>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
-    return two ? launch_bf16<64, 2>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
-               : launch_bf16<64, 1>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+      return two ? launch_bf16<128, 2>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+                 : launch_bf16<128, 1>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+    return two ? launch_bf16<64, 2>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+               : launch_bf16<64, 1>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
   }
-  return dh == 128 ? launch_f32<128>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out)
-                   : launch_f32<64>(st, t, B, nh, L, sc, q, k_tree, v_tree, k_cache, v_cache, out);
+  return dh == 128 ? launch_f32<128>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out)
+                   : launch_f32<64>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out);
+}
+
+}  // namespace
+
+extern "C" medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                                        int B, int nh, int dh, int L, float scale, const void *q,
+                                        const void *k_tree, const void *v_tree, const void *k_cache,
+                                        const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+  return attention_entry("tree_attention", stream, dt, t, B, nh, dh, Prefix{L, L, nullptr}, scale, q, k_tree,
+                         v_tree, k_cache, v_cache, out, ws, ws_bytes);
+}
+
+extern "C" medusa_status tree_attention_ragged(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
+                                               int B, int nh, int dh, int L_cap, int L_max,
+                                               const int32_t *seq_len, float scale, const void *q,
+                                               const void *k_tree, const void *v_tree, const void *k_cache,
+                                               const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+  if (!seq_len) return fail(MEDUSA_ERR_ARG, "tree_attention_ragged: NULL seq_len");
+  if (L_max > L_cap) return fail(MEDUSA_ERR_ARG, "tree_attention_ragged: L_max=%d > L_cap=%d", L_max, L_cap);
+  return attention_entry("tree_attention_ragged", stream, dt, t, B, nh, dh, Prefix{L_max, L_cap, seq_len}, scale,
+                         q, k_tree, v_tree, k_cache, v_cache, out, ws, ws_bytes);
 }

@@ -33,34 +33,39 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;          // reduction tile (two MFMA k-steps)
-constexpr int kLdk = kBK + 8;    // padded LDS row, elements (144 bytes)
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int BN, int BM, int WGN, int WGM>
+// BK: reduction tile (BK/32 MFMA k-steps); LDS rows padded by 16 bytes
+template <int BN, int BM, int WGN, int WGM, int BK>
 struct TileShape {
   static constexpr int kThreads = 64 * WGN * WGM;
+  static constexpr int kLdk = BK + 8;                  // padded LDS row, elements
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per row per k-tile
+  static constexpr int SPT = BK / 32;                  // MFMA k-steps per k-tile
   static constexpr int TN = BN / WGN, TM = BM / WGM;   // wave sub-tile
   static constexpr int FN = TN / 16, FM = TM / 16;     // MFMA tiles per wave
-  static constexpr int WCH = BN * 8 / kThreads;        // 16-byte chunks per thread per k-tile
-  static constexpr int XCH = BM * 8 / kThreads;
+  static constexpr int WCH = BN * CPR / kThreads;      // chunks per thread per k-tile
+  static constexpr int XCH = BM * CPR / kThreads;
   static constexpr int kStage = (BN + BM) * kLdk;      // elements per LDS stage
   static constexpr size_t kLdsBytes = 2 * kStage * sizeof(uint16_t);
+  static_assert(BK == 32 || BK == 64, "k-tile");
   static_assert(TN % 16 == 0 && TM % 16 == 0, "wave tile");
-  static_assert((BN * 8) % kThreads == 0 && (BM * 8) % kThreads == 0, "load split");
+  static_assert((BN * CPR) % kThreads == 0 && (BM * CPR) % kThreads == 0, "load split");
+  static_assert((kThreads / 64) % SPT == 0 && kThreads % CPR == 0, "affine slots");
   static_assert(BN % 16 == 0, "packed tiles");
 };
 
-template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM>
-__global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
+template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM, int BK, int MINW>
+__global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
     int H, int M, int GM, const uint16_t *__restrict__ resid, uint16_t *__restrict__ out_bf16,
     float *__restrict__ out_f32) {
-  using S = TileShape<BN, BM, WGN, WGM>;
+  using S = TileShape<BN, BM, WGN, WGM, BK>;
+  constexpr int kLdk = S::kLdk;
   extern __shared__ u32x4_t lds_raw[];
   uint16_t *lds = reinterpret_cast<uint16_t *>(lds_raw);
 
@@ -93,34 +98,37 @@ __global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
   for (int j = 0; j < S::WCH; ++j) {
     const int c = tid + j * S::kThreads;
     if (PACKED) {
-      // slot c: lane c%64 of fragment (row tile c/128, k-step (c/64)%2)
-      const int t = min(n0 / 16 + (c >> 7), NTt - 1);
-      woff[j] = ((uint32_t)(t * Ssteps + ((c >> 6) & 1)) * 64u + (uint32_t)(c & 63)) * 16u;
+      // slot c: lane c%64 of fragment F = c/64: row tile F/SPT, k-step F%SPT
+      const int F = c >> 6;
+      const int t = min(n0 / 16 + F / S::SPT, NTt - 1);
+      woff[j] = ((uint32_t)(t * Ssteps + F % S::SPT) * 64u + (uint32_t)(c & 63)) * 16u;
     } else {
-      // slot c: row c/8, columns 8*(c%8)..+7 (each row's 128 bytes in 8 lanes)
-      const int n = min(n0 + (c >> 3), N - 1);
-      woff[j] = ((uint32_t)n * (uint32_t)H + (uint32_t)(c & 7) * 8u) * 2u;
+      // slot c: row c/CPR, columns 8*(c%CPR)..+7 (each row's k-tile in CPR lanes)
+      const int n = min(n0 + c / S::CPR, N - 1);
+      woff[j] = ((uint32_t)n * (uint32_t)H + (uint32_t)(c % S::CPR) * 8u) * 2u;
     }
   }
 #pragma unroll
   for (int j = 0; j < S::XCH; ++j) {
     const int c = tid + j * S::kThreads;
-    const int m = min(m0 + (c >> 3), M - 1);
-    xoff[j] = ((uint32_t)m * (uint32_t)H + (uint32_t)(c & 7) * 8u) * 2u;
+    const int m = min(m0 + c / S::CPR, M - 1);
+    xoff[j] = ((uint32_t)m * (uint32_t)H + (uint32_t)(c % S::CPR) * 8u) * 2u;
   }
-  // LDS destinations (elements): packed slot -> row 16*(c/128) + l%16, column
-  // 32*((c/64)%2) + 8*(l/16) with l = c%64; row-major slot -> row c/8, column 8*(c%8)
-  constexpr int kWdstStep = PACKED ? (S::kThreads / 128) * 16 * kLdk : (S::kThreads / 8) * kLdk;
-  const int wdst0 = PACKED ? ((tid >> 7) * 16 + (tid & 15)) * kLdk + ((tid >> 6) & 1) * 32 + ((tid >> 4) & 3) * 8
-                           : (tid >> 3) * kLdk + (tid & 7) * 8;
-  const int xdst0 = BN * kLdk + (tid >> 3) * kLdk + (tid & 7) * 8;
-  constexpr int kXdstStep = (S::kThreads / 8) * kLdk;
-  const uint32_t w_step = PACKED ? 2u * 1024u : kBK * 2u;   // bytes per k-tile
+  // LDS destinations (elements): packed slot -> row 16*(F/SPT) + l%16, column
+  // 32*(F%SPT) + 8*(l/16) with F = c/64, l = c%64; row-major slot -> row c/CPR,
+  // column 8*(c%CPR)
+  constexpr int kWdstStep = PACKED ? (S::kThreads / 64 / S::SPT) * 16 * kLdk : (S::kThreads / S::CPR) * kLdk;
+  const int wdst0 = PACKED ? (((tid >> 6) / S::SPT) * 16 + (tid & 15)) * kLdk + ((tid >> 6) % S::SPT) * 32 +
+                                 ((tid >> 4) & 3) * 8
+                           : (tid / S::CPR) * kLdk + (tid % S::CPR) * 8;
+  const int xdst0 = BN * kLdk + (tid / S::CPR) * kLdk + (tid % S::CPR) * 8;
+  constexpr int kXdstStep = (S::kThreads / S::CPR) * kLdk;
+  const uint32_t w_step = PACKED ? S::SPT * 1024u : BK * 2u;   // bytes per k-tile
 
   // two register sets: tile j is loaded into set j % 2
   u32x4_t wreg[2][S::WCH], xreg[2][S::XCH];
   auto load = [&](int kt, int set) {
-    const uint32_t wk = (uint32_t)kt * w_step, xk = (uint32_t)kt * (kBK * 2u);
+    const uint32_t wk = (uint32_t)kt * w_step, xk = (uint32_t)kt * (BK * 2u);
 #pragma unroll
     for (int j = 0; j < S::WCH; ++j) wreg[set][j] = *reinterpret_cast<const u32x4_t *>(wbase + (woff[j] + wk));
 #pragma unroll
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
   auto compute = [&](int stage) {
     const uint16_t *base = lds + stage * S::kStage;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
+    for (int ks = 0; ks < S::SPT; ++ks) {
       u32x4_t a[S::FN], b[S::FM];
 #pragma unroll
       for (int f = 0; f < S::FN; ++f) a[f] = *reinterpret_cast<const u32x4_t *>(base + a_off + f * 16 * kLdk + ks * 32);
@@ -159,13 +167,13 @@ __global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
     }
   };
 
-  // Software pipeline, two k-tiles per trip (H % 128 == 0, so nk is even):
+  // Software pipeline, two k-tiles per trip (H % (2*BK) == 0, so nk is even):
   // while stage s feeds the MFMAs, tile kt+1 waits in registers (loaded one
   // compute phase earlier) and tile kt+2 is being loaded, so every global
   // load has two compute phases to arrive.  Loads past the end re-read the
   // last tile into a stage that is never read again, keeping the trip
   // branch-free.
-  const int nk = H / kBK;
+  const int nk = H / BK;
   load(0, 0);
   load(min(1, nk - 1), 1);
   stash(0, 0);
@@ -219,11 +227,12 @@ __global__ __launch_bounds__(64 * WGN * WGM, 1) void head_gemm_tiled(
   }
 }
 
-template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM>
+template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM, int BK, int MINW>
 medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N,
                            int H, int M, int GM, const uint16_t *resid, uint16_t *ob, float *of) {
-  using S = TileShape<BN, BM, WGN, WGM>;
-  auto kern = head_gemm_tiled<EPI, PACKED, BN, BM, WGN, WGM>;
+  using S = TileShape<BN, BM, WGN, WGM, BK>;
+  if (H % (2 * BK) != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% %d != 0 (H=%d)", 2 * BK, H);
+  auto kern = head_gemm_tiled<EPI, PACKED, BN, BM, WGN, WGM, BK, MINW>;
   static bool attr_set = false;   // per instantiation; setting it twice is harmless
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -245,11 +254,10 @@ namespace medusa {
 template <int EPI, bool PACKED>
 medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                                   int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  if (H % kBK != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% %d != 0 (H=%d)", kBK, H);
   const size_t w_head = PACKED ? (size_t)((N + 15) / 16) * (H / 32) * 1024 : (size_t)N * H * 2;
   if (w_head >= (1ull << 32) || (size_t)M * H * 2 >= (1ull << 32))
     return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
-  return launch_tiled<EPI, PACKED, 256, 256, 2, 4>(st, W, X, xhs, K, N, H, M, 8, resid, ob, of);
+  return launch_tiled<EPI, PACKED, 256, 256, 2, 4, 64, 1>(st, W, X, xhs, K, N, H, M, 8, resid, ob, of);
 }
 
 template medusa_status head_gemm_many_rows<kEpiResblock, false>(hipStream_t, const uint16_t *, const uint16_t *,
