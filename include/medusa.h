@@ -14,6 +14,7 @@
  *       medusa_tree_tokens  the token of every tree node
  *   (3) tree_attention      every node over the prefix KV cache + its ancestors
  *   (4) typical_accept      typical acceptance and the longest accepted prefix
+ *       rejection_accept    the rejection-sampling rule it is compared with
  *   (5) medusa_kv_commit    append the accepted path to the KV cache
  *
  * Conventions (all calls):
@@ -262,6 +263,34 @@ medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B
                              float delta, float temperature, int32_t *accept_len,
                              int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
                              float *cand_p, float *row_thr, void *ws, size_t ws_bytes);
+
+/* (4b) Rejection-sampling acceptance, the rule typical acceptance replaces
+ *     (paper summary, "两个扩展" and "关键发现"; the pages name it without
+ *     spelling it out).  Starting at the root (always kept), the children of
+ *     the current node u are tried in rank order: child c with token x is kept
+ *     iff u_node[b][c] < min(1, p(x) / q(x)), p = softmax(logits[b][u] / T)
+ *     (after the updates of the siblings rejected before c) and q =
+ *     softmax(head_logits[depth(u)][b] / T), the head that drafted c; a
+ *     rejected child replaces p by max(0, p - q) renormalised (kept as is if
+ *     that is zero).  The first kept child becomes u.  With no child kept, or
+ *     at a leaf, the next token is the inverse-CDF draw from the current p at
+ *     u_bonus[b]: the smallest v with p(0) + ... + p(v) > u_bonus * sum(p).
+ *     temperature 0: one-hot p and q at the argmax (lowest id) -- greedy
+ *     verification.  Tokens outside [0, V) are never kept.
+ *  logits      [B][T][V] device float   verification logits at every node
+ *  head_logits [K][B][V] device float   the heads' logits (K >= depth_max)
+ *  tree_tok    [B][T]    device int32
+ *  u_node [B][T], u_bonus [B]  device float, uniforms in [0, 1) (u_node[b][0]
+ *                              is not used)
+ *  accept_len, best_node, next_tok [B], accepted_tok [B][depth_max+1]: as
+ *  typical_accept.  keep_prob [B][T] device float, optional (NULL): the
+ *  keep probability of every tried child, nan elsewhere.
+ *  Errors: ERR_SHAPE (K < depth_max), ERR_ARG. */
+medusa_status rejection_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V, int K,
+                               const float *logits, const float *head_logits, const int32_t *tree_tok,
+                               float temperature, const float *u_node, const float *u_bonus,
+                               int32_t *accept_len, int32_t *best_node, int32_t *next_tok,
+                               int32_t *accepted_tok, float *keep_prob);
 
 /* ------------------------------------------------------------------------- */
 /* (5) KV-cache commit.  Paper summary, "基准/方法设计" (the accepted prefix

@@ -430,6 +430,102 @@ def typical_accept(logits, tree_tok, tree, eps, delta, temperature=1.0):
 
 
 # ----------------------------------------------------------------------------
+# (4b) rejection-sampling acceptance -- [P3] "两个扩展" and "关键发现":
+#      typical acceptance is presented as the replacement for rejection
+#      sampling (the comparison point); the pages do not spell the rule out.
+# ----------------------------------------------------------------------------
+def rs_accept_prob(p, q, x):
+    """Probability of keeping a drafted token x: min(1, p(x) / q(x)), with
+    p the target (verification) distribution and q the draft (head)
+    distribution; q(x) = 0 keeps x iff p(x) > 0."""
+    px, qx = float(p[x]), float(q[x])
+    if qx == 0.0:
+        return 1.0 if px > 0.0 else 0.0
+    return min(1.0, px / qx)
+
+
+def rs_residual(p, q):
+    """Target after a rejected draft: max(0, p - q), renormalised.  When p <= q
+    everywhere (then every draft is kept with probability 1, so a rejection
+    cannot have happened) p is returned unchanged."""
+    r = np.maximum(p - q, 0.0)
+    Z = r.sum()
+    return r / Z if Z > 0.0 else p
+
+
+def sample_inverse_cdf(p, u):
+    """Smallest token v with sum_{w <= v} p(w) > u * sum(p) (u in [0, 1)); the
+    last token of nonzero probability if rounding leaves none."""
+    c = np.cumsum(p)
+    hit = np.flatnonzero(c > u * c[-1])
+    return int(hit[0]) if hit.size else int(np.flatnonzero(p > 0)[-1])
+
+
+def rejection_accept(logits, head_logits, tree_tok, tree, temperature, u_node, u_bonus):
+    """Rejection-sampling acceptance over the candidate tree, per sequence.
+
+    Reading (the standard speculative-sampling rule, extended to several
+    drafts per node by testing siblings one after the other against the
+    residual of the rejected ones): starting at the root (always kept), the
+    children of the current node u are tried in rank order; child c with
+    token x is kept iff u_node[b][c] < min(1, p(x) / q(x)), where p is the
+    verification distribution at u (after the residual updates of the
+    siblings rejected before c) and q is the distribution of the head that
+    drafted c's depth (head depth(u), softmax of head_logits[depth(u)][b]),
+    both at the given temperature.  A rejected sibling replaces p by
+    rs_residual(p, q).  The first kept child becomes u; when none is kept, or
+    u is a leaf, the step ends and the next token is sampled by inverse CDF
+    with u_bonus[b] from the current p (the residual after all of u's
+    children were rejected, else u's own distribution).  temperature 0 uses
+    one-hot distributions at the argmax (lowest index), which makes this
+    greedy verification.
+
+    logits [B][T][V]; head_logits [K][B][V]; tree_tok [B][T];
+    u_node [B][T], u_bonus [B] in [0, 1).
+    Returns accept_len, best, next_tok, accepted_tok (as typical_accept) and
+    a [B][T]: the keep probability of every tested node (nan elsewhere).
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    head_logits = np.asarray(head_logits, dtype=np.float64)
+    B, T, V = logits.shape
+    parent, depth = tree["parent"], tree["depth"]
+    Dm = tree["depth_max"]
+    children = [[] for _ in range(T)]
+    for c in range(1, T):
+        children[parent[c]].append(c)            # increasing index = rank order
+    res = {
+        "accept_len": np.zeros(B, np.int64), "best": np.zeros(B, np.int64),
+        "next_tok": np.zeros(B, np.int64),
+        "accepted_tok": np.full((B, Dm + 1), -1, np.int64),
+        "a": np.full((B, T), np.nan),
+    }
+    for b in range(B):
+        u, chain = 0, [0]
+        while True:
+            p, _, _ = row_distribution(logits[b, u], temperature)
+            if not children[u]:
+                break
+            q, _, _ = row_distribution(head_logits[depth[u], b], temperature)
+            kept = None
+            for c in children[u]:
+                a = rs_accept_prob(p, q, int(tree_tok[b, c]))
+                res["a"][b, c] = a
+                if u_node[b, c] < a:
+                    kept = c
+                    break
+                p = rs_residual(p, q)
+            if kept is None:
+                break
+            u = kept
+            chain.append(u)
+        res["accept_len"][b] = depth[u]
+        res["best"][b] = u
+        res["accepted_tok"][b, :len(chain)] = np.asarray(tree_tok)[b, chain]
+        res["next_tok"][b] = sample_inverse_cdf(p, float(u_bonus[b]))
+    return res
+
+
+# ----------------------------------------------------------------------------
 # (5) KV-cache commit -- [P3] "基准/方法设计" (the next round starts after the
 #     accepted prefix), [P2] "部署与生成" (generation keeps the KV cache)
 # ----------------------------------------------------------------------------

@@ -59,6 +59,7 @@ SIGNATURES = {
     "tree_attention": (_i, [_p, _i, _p, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "tree_attention_ragged": (_i, [_p, _i, _p, _i, _i, _i, _i, _i, _p, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "medusa_kv_commit": (_i, [_p, _i, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "rejection_accept": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p]),
     "typical_accept_workspace": (_sz, [_p, _i, _i]),
     "typical_accept": (_i, [_p, _p, _i, _i, _p, _p, _f, _f, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
 }
@@ -348,3 +349,14 @@ def typical_accept(tree, logits, tree_tok, eps, delta, temperature, accept_len, 
                              float(delta), float(temperature), _ptr(accept_len), _ptr(best_node),
                              _ptr(next_tok), _ptr(accepted_tok), _ptr(cand_p), _ptr(row_thr), _ptr(ws),
                              ws.numel()))
+
+
+def rejection_accept(tree, logits, head_logits, tree_tok, temperature, u_node, u_bonus, accept_len, best_node,
+                     next_tok, accepted_tok, keep_prob=None):
+    """Rejection-sampling acceptance: logits [B][T][V], head_logits [K][B][V],
+    uniforms u_node [B][T] and u_bonus [B]."""
+    _dev(logits, head_logits, tree_tok, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob)
+    B, T, V = logits.shape
+    check(lib.rejection_accept(_stream(), tree.handle, B, V, head_logits.shape[0], _ptr(logits), _ptr(head_logits),
+                               _ptr(tree_tok), float(temperature), _ptr(u_node), _ptr(u_bonus), _ptr(accept_len),
+                               _ptr(best_node), _ptr(next_tok), _ptr(accepted_tok), _ptr(keep_prob)))

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmedusa_hip.so")
-SOURCES = ["host.hip", "heads.hip", "gemm.hip", "topk.hip", "attention.hip", "accept.hip", "commit.hip"]
+SOURCES = ["host.hip", "heads.hip", "gemm.hip", "topk.hip", "attention.hip", "accept.hip", "rejection.hip", "commit.hip"]
 ARCH = "gfx950"
 
 
