@@ -121,6 +121,135 @@ def verify_pass(s, reps):
     return out
 
 
+def time_steps(s, n, warmup, copies=1):
+    """Average us of a whole step over n steps, and per-stage us from a
+    separate instrumented pass (events between stages)."""
+    import torch
+    for i in range(warmup):
+        s.run(i % copies)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        s.run(i % copies)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / n
+    names = ["head_resblock", "head_vocab", "topk_tokens", "attention", "accept"]
+    fns = [s.heads, s.heads_vocab, s.topk_and_tokens, s.attention, s.accept]
+    reps = min(n, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        for j, fn in enumerate(fns):
+            fn(i % copies)
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    stage = {nm: 1e3 * sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(reps)) / reps
+             for j, nm in enumerate(names)}
+    return us, stage
+
+
+def tree_sweep(cfg, args):
+    """Step time against tree size at the workload's shapes: greedy sparse
+    trees of 16..256 nodes and dense trees of about 256 and 340 candidates
+    (the acceptance side of the comparison needs a trained model)."""
+    import dataclasses
+    import torch
+    from speculative_decoding_05_amd import binding as mb
+    from speculative_decoding_05_amd import configs, synth
+    from speculative_decoding_05_amd import step as st
+    base_tree = st.build_tree(cfg)
+    base = st.Step(cfg, base_tree, st.host_inputs(cfg, base_tree.T))
+    variants = [("greedy", n) for n in (15, 31, 63, 127, 255)] + [("dense", (3, 6)), ("dense", (4, 4))]
+    for kind, arg in variants:
+        if kind == "greedy":
+            spec = configs.TreeSpec("greedy", k=10, n_paths=arg, rank_cap=10)
+            c2 = dataclasses.replace(cfg, tree=spec)
+            tree = st.build_tree(c2)
+        else:
+            depth, k = arg
+            spec = configs.TreeSpec("dense", k=k)
+            c2 = dataclasses.replace(cfg, tree=spec)
+            tree = mb.Tree(mb.dense_paths(depth, k), cfg.K, k).upload()
+        host = {"h": synth.hidden(c2), "root_tok": synth.root_tokens(c2)}
+        host["q"], host["kt"], host["vt"] = synth.tree_qkv(c2, tree.T)
+        host["kc"], host["vc"] = synth.kv_cache(c2)
+        s2 = st.Step(c2, tree, host, weights_of=base)
+        s2.heads()
+        s2.heads_vocab()
+        s2.topk_and_tokens()
+        torch.cuda.synchronize()
+        s2.set_verify_logits(st.verify_logits_for(c2, tree, s2.topk_idx.cpu().numpy(), host["root_tok"]))
+        us, stage = time_steps(s2, args.steps, args.warmup)
+        print(json.dumps({"sweep": "trees", "workload": cfg.name, "tree": kind, "T": tree.T, "k": spec.k,
+                          "depth_max": tree.depth_max, "us_per_step": us, "stage_us": stage}), flush=True)
+        del s2
+        torch.cuda.empty_cache()
+
+
+def accept_sweep(cfg, args, n_seq=32):
+    """Synthetic accept-length curves on the workload's tree: typical
+    acceptance against its threshold eps (0.01..0.25) and against the
+    temperature, rejection sampling against the temperature.  Candidates are
+    the library's top-k of seeded head logits; verification logits are planted
+    at them; uniforms are seeded.  Mean accepted candidates per step."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from speculative_decoding_05_amd import binding as mb
+    from speculative_decoding_05_amd import step as st
+    from speculative_decoding_05_amd import synth
+    c2 = dataclasses.replace(cfg, B=n_seq)
+    tree = st.build_tree(c2)
+    B, T, V, K, k = n_seq, tree.T, cfg.V, cfg.K, cfg.k
+    g = torch.Generator(device="cuda").manual_seed(cfg.cfg_id)
+    head = torch.randn((K, B, V), generator=g, device="cuda") * 2.5
+    root = torch.from_numpy(synth.root_tokens(c2)).cuda()
+    idx = torch.empty((K, B, k), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, T), dtype=torch.int32, device="cuda")
+    mb.medusa_topk_tree_tokens(tree, head, k, root, idx, tok)
+    torch.cuda.synchronize()
+    vl = torch.from_numpy(st.verify_logits_for(c2, tree, idx.cpu().numpy(), root.cpu().numpy())).cuda()
+    ur = np.random.default_rng(cfg.cfg_id * 7919)
+    u_node = torch.from_numpy(ur.random((B, T)).astype(np.float32)).cuda()
+    u_bonus = torch.from_numpy(ur.random(B).astype(np.float32)).cuda()
+    out = {n: torch.empty(B, dtype=torch.int32, device="cuda") for n in ("len", "best", "next")}
+    acc = torch.empty((B, tree.depth_max + 1), dtype=torch.int32, device="cuda")
+    ws = mb.workspace(mb.typical_accept_workspace(tree, B, V))
+
+    def typical(eps, tau):
+        mb.typical_accept(tree, vl, tok, eps, cfg.delta, tau, out["len"], out["best"], out["next"], acc, ws=ws)
+
+    def rejection(tau):
+        mb.rejection_accept(tree, vl, head, tok, tau, u_node, u_bonus, out["len"], out["best"], out["next"], acc)
+
+    def mean_len(fn):
+        fn()
+        return float(out["len"].float().mean().item())
+
+    def time_us(fn, n=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    res = {"sweep": "accept", "workload": cfg.name, "sequences": B, "tree_nodes": T, "delta": cfg.delta,
+           "eps_curve": [[e, mean_len(lambda: typical(e, 1.0))] for e in (0.01, 0.03, 0.05, 0.09, 0.15, 0.25)],
+           "temperature_curve": {
+               "typical": [[t, mean_len(lambda: typical(cfg.eps, t))] for t in (0.0, 0.25, 0.5, 0.7, 1.0, 1.5, 2.0)],
+               "rejection": [[t, mean_len(lambda: rejection(t))] for t in (0.0, 0.25, 0.5, 0.7, 1.0, 1.5, 2.0)]},
+           "us_per_call": {"typical": time_us(lambda: typical(cfg.eps, 1.0)),
+                           "rejection": time_us(lambda: rejection(1.0))},
+           "data": "synthetic: seeded head logits, verification logits planted at their top-k, seeded uniforms"}
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(nbytes):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -178,6 +307,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle time budget (0: skip)")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="bytes of rotated per-step inputs")
     ap.add_argument("--copy-probe", type=int, default=0, help="only copy this many bytes (counter calibration)")
+    ap.add_argument("--sweep", choices=["trees", "accept"], default=None,
+                    help="instead of the headline line: step time per tree size, or acceptance curves")
     ap.add_argument("--verify-reps", type=int, default=5,
                     help="repetitions of each verify-pass contraction (0: skip)")
     ap.add_argument("--event-every", type=int, default=8,
@@ -195,6 +326,12 @@ def main():
         b.build()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.sweep:
+        from speculative_decoding_05_amd import configs as _c
+        torch.cuda.set_device(0)
+        cfg = _c.CONFIGS[args.config]
+        (tree_sweep if args.sweep == "trees" else accept_sweep)(cfg, args)
         return
     from speculative_decoding_05_amd import configs
     from speculative_decoding_05_amd import step as st

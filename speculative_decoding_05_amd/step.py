@@ -39,20 +39,25 @@ class Step:
     rotate through them and not be served from the last-level cache.
     """
 
-    def __init__(self, cfg: configs.Config, tree: mb.Tree, host: dict, copies: int = 1, device="cuda"):
+    def __init__(self, cfg: configs.Config, tree: mb.Tree, host: dict, copies: int = 1, device="cuda",
+                 weights_of: "Step | None" = None):
         self.cfg, self.tree, self.copies = cfg, tree, copies
         B, K, V, H, k, T = cfg.B, cfg.K, cfg.V, cfg.H, cfg.k, tree.T
         dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.dt = dt
         dev = device
-        self.W1 = to_device(host["W1"], dev)
-        self.W2 = to_device(host["W2"], dev)
         self.packed = cfg.dtype == "bf16"
-        if self.packed:  # one-time reorder into the matrix-core fragment order
-            self.W1p = mb.PackedWeights(self.W1)
-            self.W2p = mb.PackedWeights(self.W2)
-            torch.cuda.synchronize()
-            del self.W1, self.W2
+        if weights_of is not None:  # share another step's (identically shaped) head weights
+            for name in ("W1p", "W2p") if self.packed else ("W1", "W2"):
+                setattr(self, name, getattr(weights_of, name))
+        else:
+            self.W1 = to_device(host["W1"], dev)
+            self.W2 = to_device(host["W2"], dev)
+            if self.packed:  # one-time reorder into the matrix-core fragment order
+                self.W1p = mb.PackedWeights(self.W1)
+                self.W2p = mb.PackedWeights(self.W2)
+                torch.cuda.synchronize()
+                del self.W1, self.W2
         self.root = to_device(host["root_tok"].astype(np.int32), dev)
         self.h = [to_device(host["h"], dev) for _ in range(copies)]
         self.q = [to_device(host["q"], dev) for _ in range(copies)]
