@@ -43,6 +43,7 @@ constexpr int kPadV = 16;      // row padding (bf16) of the V tile: 8 rows of a 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMinKeysPerSplit = 256;
 constexpr int kSplitTargetBlocks = 128;
+constexpr long kCUs = 256;     // compute units of the device
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -71,18 +72,26 @@ struct Split {
 // Query tiles per wave: two once the tree has more than 64 tokens.
 inline int qtiles_for(int T) { return T > kQB ? 2 : 1; }
 
-inline Split choose_split(int B, int nh, int T, int L) {
-  const int qb = kQB * qtiles_for(T);
-  const long pairs = (long)B * nh * ((T + qb - 1) / qb);
-  int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
-  const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
-  if (ns > max_ns) ns = max_ns;
+// ns slices of whole key tiles covering L keys (fewer if the tiles run out)
+inline Split split_into(int L, int ns) {
   if (ns < 1) ns = 1;
   int per = (L + ns - 1) / ns;
   per = (per + kKT - 1) / kKT * kKT;
   if (per == 0) per = kKT;
   ns = L > 0 ? (L + per - 1) / per : 1;
   return {ns, per};
+}
+
+inline Split choose_split(int B, int nh, int T, int L) {
+  const int qb = kQB * qtiles_for(T);
+  const long pairs = (long)B * nh * ((T + qb - 1) / qb);
+  int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
+  // between one and two blocks per CU, the CUs that get two set the time;
+  // three slices even the load out (measured: 13B shape, 320 pairs, 4096 keys)
+  if (pairs > kCUs && pairs < 2 * kCUs) ns = 3;
+  const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
+  if (ns > max_ns) ns = max_ns;
+  return split_into(L, ns);
 }
 
 template <int DH>
@@ -198,8 +207,8 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
     l_lane[qt] = 0.f;
   }
 
-  // register stages: tiles t+1 (and t+2) are in flight while tile t is consumed
-  TileRegs<DH> regs0, regs1;
+  // register stages: the next STAGES tiles are in flight while one is consumed
+  TileRegs<DH> regs[STAGES];
   auto fetch = [&](TileRegs<DH> &r, int tile) {
     if (tile < ncache)
       load_tile<DH>(r, kc_bh, vc_bh, cache_stride, c0 + tile * kKT, c1);
@@ -298,31 +307,22 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
       }
     }
   };
-  if (STAGES == 2) {
-    if (ntiles > 0) fetch(regs0, 0);
-    if (ntiles > 1) fetch(regs1, 1);
-    for (int tile = 0; tile < ntiles; tile += 2) {
-      __syncthreads();  // previous tile fully consumed
-      store_tile<DH>(regs0, ks, vs);
-      __syncthreads();
-      if (tile + 2 < ntiles) fetch(regs0, tile + 2);
-      consume(tile);
-      if (tile + 1 < ntiles) {
+  // tile j waits in register stage j % STAGES; it is fetched STAGES tiles
+  // before it is stored to LDS and consumed
+#pragma unroll
+  for (int r = 0; r < STAGES; ++r)
+    if (r < ntiles) fetch(regs[r], r);
+  for (int tile = 0; tile < ntiles; tile += STAGES) {
+#pragma unroll
+    for (int r = 0; r < STAGES; ++r) {
+      const int tj = tile + r;
+      if (tj < ntiles) {
+        __syncthreads();  // previous tile fully consumed
+        store_tile<DH>(regs[r], ks, vs);
         __syncthreads();
-        store_tile<DH>(regs1, ks, vs);
-        __syncthreads();
-        if (tile + 3 < ntiles) fetch(regs1, tile + 3);
-        consume(tile + 1);
+        if (tj + STAGES < ntiles) fetch(regs[r], tj + STAGES);
+        consume(tj);
       }
-    }
-  } else {
-    if (ntiles > 0) fetch(regs0, 0);
-    for (int tile = 0; tile < ntiles; ++tile) {
-      __syncthreads();
-      store_tile<DH>(regs0, ks, vs);
-      __syncthreads();
-      if (tile + 1 < ntiles) fetch(regs0, tile + 1);
-      consume(tile);
     }
   }
 
@@ -491,12 +491,11 @@ struct Prefix {
   const int32_t *seq_len;
 };
 
-template <int DH, int QT>
-medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, float scale,
+template <int DH, int QT, int STAGES = 1>
+medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, Split sp, float scale,
                           const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                           const void *v_cache, void *out, void *ws) {
   const int L = pf.L;
-  const Split sp = choose_split(B, nh, t->T, L);
   const int qgroups = (t->T + kQB * QT - 1) / (kQB * QT);
   const long nblocks = (long)B * nh * qgroups * sp.nsplit;
   if (nblocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: grid too large");
@@ -506,7 +505,7 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
     ws_o = static_cast<float *>(ws);
     ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
   }
-  hipLaunchKernelGGL((tree_attn_bf16<DH, QT, QT == 1 ? 2 : 1>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
+  hipLaunchKernelGGL((tree_attn_bf16<DH, QT, STAGES>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
                      t->W, L, pf.Lstride, pf.seq_len, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
@@ -570,11 +569,12 @@ medusa_status attention_entry(const char *who, medusa_stream_t stream, medusa_dt
   hipStream_t st = as_stream(stream);
   if (dt == MEDUSA_BF16) {
     const bool two = qtiles_for(t->T) == 2;
+    const Split sp = choose_split(B, nh, t->T, L);
     if (dh == 128)
-      return two ? launch_bf16<128, 2>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
-                 : launch_bf16<128, 1>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
-    return two ? launch_bf16<64, 2>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
-               : launch_bf16<64, 1>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+      return two ? launch_bf16<128, 2>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+                 : launch_bf16<128, 1>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+    return two ? launch_bf16<64, 2>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+               : launch_bf16<64, 1>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
   }
   return dh == 128 ? launch_f32<128>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out)
                    : launch_f32<64>(st, t, B, nh, pf, sc, q, k_tree, v_tree, k_cache, v_cache, out);
