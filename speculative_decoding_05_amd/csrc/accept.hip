@@ -1,6 +1,6 @@
 // Typical acceptance over the candidate tree.
 //
-// Row pass (one block per 4096- or 16384-wide chunk of the verification row of a node
+// Row pass (one block per 4096-wide chunk of the verification row of a node
 // that has children): every thread folds its 16 values into running
 // statistics of y = z / temperature -- max m, S = sum e^(y-m),
 // E = sum e^(y-m) (y-m) -- and the argmax of z (lowest index on ties); one
@@ -24,9 +24,8 @@ namespace {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;                  // row pass
-constexpr int kVecNarrow = 4;                  // float4 per thread: 4096-wide chunks
-constexpr int kVecWide = 16;                   // 16384-wide chunks when many rows (measured)
-constexpr long kWideRows = 2048;               // rows at which the wide chunks win
+constexpr int kVec = 4;                        // float4 per thread: 4096-wide chunks (measured
+                                               // faster than 16384-wide ones at every shape)
 constexpr int kScanThreads = 512;              // scan
 constexpr int kBatch = 8;                      // independent loads issued together
 constexpr float kLog2e = 1.4426950408889634f;
@@ -114,35 +113,58 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
   const int row = internal[slot];
   const float *z = logits + ((size_t)b * T + row) * V;
   const int base = chunk * kThreads * VEC * 4;
-  const bool vec_ok = (V % 4) == 0;
-  float val[VEC][4];
+  // argmax as the values arrive: a thread visits its indices in increasing
+  // order, so only a strictly larger value moves it (the first maximum stays)
   Stat st = empty_stat();
-#pragma unroll
-  for (int u = 0; u < VEC; ++u) {
+  float val[VEC][4];
+  auto note = [&](int u) {
     const int i0 = base + (u * kThreads + threadIdx.x) * 4;
-    if (vec_ok && i0 + 3 < V) {
-      const f32x4_t f = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(z + i0));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) val[u][j] = f[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) val[u][j] = i0 + j < V ? z[i0 + j] : -INFINITY;
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (i0 + j < V) arg_better(st.av, st.ai, val[u][j], i0 + j);
+      if (val[u][j] > st.av || (u == 0 && j == 0)) {
+        st.av = val[u][j];
+        st.ai = i0 + j;
+      }
+  };
+  if ((V % 4) == 0 && base + kThreads * VEC * 4 <= V) {   // a whole chunk: unconditional loads
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+      const f32x4_t f = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t *>(z + base + (u * kThreads + threadIdx.x) * 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) val[u][j] = f[j];
+      note(u);
+    }
+  } else {  // the row's tail chunk: element loads at clamped indices, -inf past the end
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + (u * kThreads + threadIdx.x) * 4 + j;
+        const float x = z[min(i, V - 1)];
+        val[u][j] = i < V ? x : -INFINITY;
+      }
+      note(u);
+    }
   }
   if (!greedy && st.av != -INFINITY) {
     st.m = st.av * inv_tau;  // max of y (tau > 0 keeps the order)
+    // in base 2: d2 = (y - m) log2(e); e = 2^d2; E accumulates e*d2 and is
+    // brought back to natural units once (padding and -inf give e = 0, and
+    // the clamp keeps 0 * d2 finite)
+    const float c = inv_tau * kLog2e, m2 = st.m * kLog2e;
+    float S = 0.f, E2 = 0.f;
 #pragma unroll
     for (int u = 0; u < VEC; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float d = val[u][j] * inv_tau - st.m;  // -inf for padding
-        const float e = exp2f(d * kLog2e);
-        st.S += e;
-        st.E += e == 0.f ? 0.f : e * d;
+        const float d2 = fmaf(val[u][j], c, -m2);
+        const float e = __builtin_amdgcn_exp2f(d2);
+        S += e;
+        E2 = fmaf(e, fmaxf(d2, -1e30f), E2);
       }
+    st.S = S;
+    st.E = E2 * (1.0f / kLog2e);
   }
   st = block_reduce<kThreads>(st, sh);
   if (threadIdx.x == 0) {
@@ -288,14 +310,13 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   if (tid == 0) next_tok[b] = st.ai;
 }
 
-inline int vec_for(int B, int n_internal) { return (long)B * n_internal >= kWideRows ? kVecWide : kVecNarrow; }
-inline int chunks_for(int V, int vec) { return (V + kThreads * vec * 4 - 1) / (kThreads * vec * 4); }
+inline int chunks_for(int V) { return (V + kThreads * kVec * 4 - 1) / (kThreads * kVec * 4); }
 
 }  // namespace
 
 extern "C" size_t typical_accept_workspace(const medusa_tree *t, int B, int V) {
   if (!t || B < 1 || V < 1) return 0;
-  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V, vec_for(B, t->n_internal)) * sizeof(Part);
+  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V) * sizeof(Part);
 }
 
 extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
@@ -315,18 +336,13 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
   const size_t need = typical_accept_workspace(t, B, V);
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = as_stream(stream);
-  const int vec = vec_for(B, t->n_internal);
-  const int nchunks = chunks_for(V, vec);
+  const int nchunks = chunks_for(V);
   const int greedy = temperature == 0.f;
   const float inv_tau = greedy ? 1.f : 1.f / temperature;
   Part *part = static_cast<Part *>(ws);
   if (t->n_internal > 0) {
-    if (vec == kVecWide)
-      hipLaunchKernelGGL((accept_rowpass<kVecWide>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
-                         logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
-    else
-      hipLaunchKernelGGL((accept_rowpass<kVecNarrow>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
-                         logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
+    hipLaunchKernelGGL((accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
+                       logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
     s = check_launch("typical_accept row pass");
     if (s != MEDUSA_OK) return s;
   }
