@@ -250,6 +250,86 @@ def accept_sweep(cfg, args, n_seq=32):
     print(json.dumps(res), flush=True)
 
 
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_bytes": p.total_memory}
+
+
+def copy_rate(nbytes=1 << 30, reps=5):
+    """Device-to-device copy of nbytes: (read + write bytes) / time, GB/s -- the
+    measured counterpart of the 8 TB/s datasheet peak."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return rate
+
+
+def accept_histogram(s, depth_max):
+    """Accepted candidates per sequence of the batch (synthetic planted
+    verification logits; every rotated copy carries the same ones)."""
+    counts = [0] * (depth_max + 1)
+    s.run(0)
+    for a in s.accept_len.cpu().tolist():
+        counts[a] += 1
+    return counts
+
+
+def graph_variant(s, copies, steps, warmup):
+    """The same step captured once per input copy in a HIP graph and replayed;
+    every replay's outputs are compared with the eager step's on that copy."""
+    import torch
+    outs = lambda: [t.clone() for t in (s.tree_tok, s.attn, s.accept_len, s.best, s.next_tok, s.accepted)]
+    eager = []
+    for c in range(copies):
+        s.run(c)
+        eager.append(outs())
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm the launch paths off the capture
+        s.run(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s.run(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    match = True
+    for rep in range(2):               # replays with eager work and syncs between them
+        for c in range(copies):
+            graphs[c].replay()
+            torch.cuda.synchronize()
+            match &= all(torch.equal(a, b) for a, b in zip(outs(), eager[c]))
+            s.run((c + 1) % copies)
+            torch.cuda.synchronize()
+    for i in range(warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % copies].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    return {"us_per_step": us, "steps_per_s": 1e6 / us, "replays_match_eager": bool(match)}
+
+
 def copy_probe(nbytes):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -309,6 +389,7 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, help="only copy this many bytes (counter calibration)")
     ap.add_argument("--sweep", choices=["trees", "accept"], default=None,
                     help="instead of the headline line: step time per tree size, or acceptance curves")
+    ap.add_argument("--graph", type=int, default=1, help="also time the step captured in HIP graphs (0: skip)")
     ap.add_argument("--verify-reps", type=int, default=5,
                     help="repetitions of each verify-pass contraction (0: skip)")
     ap.add_argument("--event-every", type=int, default=8,
@@ -363,10 +444,15 @@ def main():
     ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in ev_steps}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # ten equal sub-intervals of the timed steps (median / best reporting)
+    n_rep = 10 if args.steps >= 10 else 1
+    rep_at = {round(r * args.steps / n_rep): torch.cuda.Event(enable_timing=True) for r in range(1, n_rep)}
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
+        if i in rep_at:
+            rep_at[i].record()
         c = i % copies
         s.heads(c)
         if i in ev:
@@ -382,6 +468,8 @@ def main():
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_end)
     ms_step = ms / args.steps
+    marks = [(0, t_start)] + sorted(rep_at.items()) + [(args.steps, t_end)]
+    rep_rates = sorted((b - a) / (ea.elapsed_time(eb) * 1e-3) for (a, ea), (b, eb) in zip(marks, marks[1:]))
     vocab_ms = sum(a.elapsed_time(bb) for a, bb in ev.values()) / len(ev)
 
     # per-stage times from a separate instrumented pass (not the timed region)
@@ -432,6 +520,14 @@ def main():
                      "bytes_per_launch": vocab_bytes, "avg_launch_us": vocab_ms * 1e3,
                      "launches_timed": len(ev)},
     }
+    res["steps_per_s_median"] = rep_rates[len(rep_rates) // 2]
+    res["steps_per_s_best"] = rep_rates[-1]
+    res["stage_gbps"] = {n: sb[n] / (stage_us[n] * 1e-6) / 1e9 for n in names}
+    res["device"] = device_info()
+    res["hbm_copy_gbps"] = copy_rate()   # device-to-device copy, read + write bytes
+    res["accept_len_histogram"] = accept_histogram(s, tree.depth_max)
+    if args.graph:
+        res["hip_graph"] = graph_variant(s, copies, args.steps, args.warmup)
     if cfg.dtype == "bf16" and args.verify_reps > 0:
         print("[bench] verify-pass contractions (M = B*T rows)", file=sys.stderr, flush=True)
         res["verify_pass"] = verify_pass(s, args.verify_reps)
