@@ -127,15 +127,23 @@ class VerifyPass:
     (a head with W1 = 0) turning the tree-attention output of `step` into
     verification logits.  Inputs are seeded device-side normals."""
 
-    def __init__(self, step: Step, seed: int = 0):
+    def __init__(self, step: Step, seed: int = 0, h_nodes: np.ndarray | None = None,
+                 W_lm: np.ndarray | None = None):
         cfg, T = step.cfg, step.tree.T
         if not step.packed:
             raise ValueError("the verify pass runs on the bf16 (packed-weight) path")
         self.step, self.M = step, cfg.B * T
         M, H, V, K = self.M, cfg.H, cfg.V, cfg.K
         g = torch.Generator(device="cuda").manual_seed(seed)
-        self.h = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
-        W_lm = (torch.randn((1, V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        # host arrays (synth bf16 bits) when given, else device-side normals
+        if h_nodes is not None:
+            self.h = to_device(h_nodes)
+        else:
+            self.h = torch.randn((M, H), generator=g, device="cuda").to(torch.bfloat16)
+        if W_lm is not None:
+            W_lm = to_device(W_lm).reshape(1, V, H)
+        else:
+            W_lm = (torch.randn((1, V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
         self.W_lm = mb.PackedWeights(W_lm)
         torch.cuda.synchronize()
         del W_lm

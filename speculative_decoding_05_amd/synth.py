@@ -20,6 +20,7 @@ import numpy as np
 SHARED = 2 ** 32 - 1
 ROLE_W1, ROLE_W2, ROLE_H, ROLE_ROOT = 1, 2, 3, 4
 ROLE_Q, ROLE_KT, ROLE_VT, ROLE_KC, ROLE_VC, ROLE_VLOGITS = 5, 6, 7, 8, 9, 10
+ROLE_NODE_H, ROLE_W_LM = 11, 12
 WEIGHT_STD = 0.02
 
 
@@ -82,6 +83,16 @@ def head_weights(cfg):
     W1 = normal(cfg.cfg_id, ROLE_W1, SHARED, (cfg.K, cfg.H, cfg.H), WEIGHT_STD, cfg.dtype, chunks=cfg.K)
     W2 = normal(cfg.cfg_id, ROLE_W2, SHARED, (cfg.K, cfg.V, cfg.H), WEIGHT_STD, cfg.dtype, chunks=cfg.K * 4)
     return W1, W2
+
+
+def node_hidden(cfg, M):
+    """Hidden states of M tree nodes [M][H] ~ N(0, 1) (the verify-pass rows)."""
+    return normal(cfg.cfg_id, ROLE_NODE_H, SHARED, (M, cfg.H), 1.0, cfg.dtype, chunks=max(1, M // 1024))
+
+
+def lm_head_weights(cfg):
+    """The backbone's LM head W_lm [V][H] ~ N(0, 0.02^2)."""
+    return normal(cfg.cfg_id, ROLE_W_LM, SHARED, (cfg.V, cfg.H), WEIGHT_STD, cfg.dtype, chunks=8)
 
 
 def hidden(cfg, B=None):

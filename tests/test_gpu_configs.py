@@ -118,3 +118,42 @@ def test_config_chain(name):
     flagged = check_accept(ot, vl, tok_o, ref_a, gpu)
     say("  accept: flagged decisions", flagged, "of", B * (ot["T"] - 1),
         "mean accept_len", float(gpu["accept_len"].mean()))
+
+
+@pytest.mark.parametrize("name", ["roofline_b16", "vicuna13b_b8"])
+def test_verify_pass_full_size(name):
+    # NEXT-1 at the workload's full shape, in the launch configuration the bench
+    # times (packed weights, M = B*T rows on the tiled kernel): sampled rows and
+    # vocabulary entries of the heads, and the LM head over the tree-attention
+    # output of sampled sequences, each against the oracle's own values
+    cfg = configs.CONFIGS[name]
+    say("verify pass", name)
+    f = synth.as_f64
+    tree = st.build_tree(cfg)
+    hostin = st.host_inputs(cfg, tree.T)
+    M = cfg.B * tree.T
+    h_nodes, W_lm = synth.node_hidden(cfg, M), synth.lm_head_weights(cfg)
+    s = st.Step(cfg, tree, hostin)
+    vp = st.VerifyPass(s, h_nodes=h_nodes, W_lm=W_lm)
+    vp.heads_resblock()
+    vp.heads_vocab()
+    s.attention()
+    vp.lm_head()
+    torch.cuda.synchronize()
+    H, V, K = cfg.H, cfg.V, cfg.K
+    g = np.random.default_rng(cfg.cfg_id + 5)
+    rows = np.sort(g.choice(M, 4, replace=False))
+    cols = np.sort(g.choice(V, 384, replace=False))
+    ref = oracle.medusa_heads(f(h_nodes[rows]), f(hostin["W1"]), f(hostin["W2"][:, cols]), round_r_bf16=True)
+    got = host(vp.logits)[:, rows][:, :, cols]
+    for k in range(K):
+        assert rel_err(got[k], ref[k]) <= TOL["bf16"], k
+    # the LM head over the oracle's own tree attention of two sequences
+    ot = oracle_tree(cfg)
+    z = host(vp.vlogits)[0].reshape(cfg.B, tree.T, V)
+    for b in (0, cfg.B - 1):
+        sl = slice(b, b + 1)
+        o_ref = oracle.tree_attention(f(hostin["q"][sl]), f(hostin["kt"][sl]), f(hostin["vt"][sl]),
+                                      f(hostin["kc"][sl]), f(hostin["vc"][sl]), ot)
+        z_ref = oracle.verification_logits(o_ref.reshape(1, tree.T, H), f(W_lm[cols]))[0]
+        assert rel_err(z[b][:, cols], z_ref) <= TOL["bf16"], b
