@@ -163,3 +163,44 @@ def test_decode_entry_points_reject_bad_arguments():
         mb.kv_commit(t, q, q, i32(B), i32(B), kc, kc, i32(B), None)
     with pytest.raises(mb.MedusaError, match="ERR_UNSUPPORTED"):
         mb.kv_commit(t, z(B, T, nh, 4), z(B, T, nh, 4), i32(B), i32(B), z(B, nh, L_cap, 4), z(B, nh, L_cap, 4))
+
+
+def test_decode_step_full_size():
+    # the batch-16 workload's shapes (64-node tree, 32 heads of 128, L = 1024):
+    # ragged attention on sampled (b, head) slices, the commit bit for bit, and
+    # the next step's attention over the committed caches
+    cfg = configs.CONFIGS["roofline_b16"]
+    p = oracle.greedy_paths(configs.acc_exact, cfg.K, cfg.tree.n_paths, cfg.tree.rank_cap)
+    ot = oracle.build_tree(p, cfg.K, cfg.tree.k)
+    t = mb.Tree(p, cfg.K, cfg.tree.k).upload()
+    B, nh, dh, T, L_cap = cfg.B, cfg.nh, cfg.dh, ot["T"], 1100
+    g = rng(77)
+    lens = g.integers(900, 1025, B).astype(np.int32)
+    lens[0], lens[-1] = 1024, 0
+    mk = lambda shape: store(g.standard_normal(shape).astype(np.float32), "bf16")
+    kc, vc = mk((B, nh, L_cap, dh)), mk((B, nh, L_cap, dh))
+    q, kt, vt = mk((B, T, nh, dh)), mk((B, T, nh, dh)), mk((B, T, nh, dh))
+    dkc, dvc, dlen = dev(kc), dev(vc), dev(lens)
+    out = torch.empty((B, T, nh, dh), dtype=torch.bfloat16, device="cuda")
+    mb.tree_attention_ragged(t, dev(q), dev(kt), dev(vt), dkc, dvc, dlen, int(lens.max()), out)
+    got = host(out)
+    f = synth.as_f64
+    sel = [(0, 0), (3, 17), (B - 1, nh - 1), (9, 5)]
+    for b, h in sel:
+        L = int(lens[b])
+        ref = oracle.tree_attention(f(q[b:b + 1]), f(kt[b:b + 1]), f(vt[b:b + 1]), f(kc[b:b + 1, :, :L]),
+                                    f(vc[b:b + 1, :, :L]), ot, None, [(0, h)])
+        assert rel_err(got[b, :, h], ref[0, :, h]) <= TOL["bf16"], (b, h)
+    best = g.integers(0, T, B).astype(np.int32)
+    mb.kv_commit(t, dev(kt), dev(vt), dev(best), dlen, dkc, dvc)
+    rk, rv, rl = oracle.kv_commit(ot, f(kt), f(vt), best, lens, f(kc), f(vc))
+    assert host(dlen).tolist() == rl.tolist()
+    assert np.array_equal(host(dkc), rk) and np.array_equal(host(dvc), rv)
+    q2 = mk((B, T, nh, dh))
+    mb.tree_attention_ragged(t, dev(q2), dev(kt), dev(vt), dkc, dvc, dlen, int(rl.max()), out)
+    got = host(out)
+    for b, h in sel:
+        L = int(rl[b])
+        ref = oracle.tree_attention(f(q2[b:b + 1]), f(kt[b:b + 1]), f(vt[b:b + 1]), rk[b:b + 1, :, :L],
+                                    rv[b:b + 1, :, :L], ot, None, [(0, h)])
+        assert rel_err(got[b, :, h], ref[0, :, h]) <= TOL["bf16"], (b, h)
