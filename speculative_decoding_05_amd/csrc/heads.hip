@@ -235,9 +235,12 @@ void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, 
 
 // Tiling by shape (measured on MI355X).  Vocabulary projection (N = V, many
 // tiles): up to 4 rows, one row tile per wave with 16 k-steps in flight;
-// more rows, two row tiles share each B fragment.  ResBlock (N = H, few
-// tiles): more waves per block split the reduction so enough loads are in
-// flight (16 waves x 4 k-steps for up to 4 rows, 8 waves otherwise).
+// 5-8 rows, two row tiles per wave; 9-32 rows, eight row tiles per wave share
+// every activation fragment (it is the activation loads, not the weight
+// stream, that limit these), with two waves splitting the reduction.
+// ResBlock (N = H, few tiles): more waves per block split the reduction so
+// enough loads are in flight (16 waves x 4 k-steps for up to 4 rows, 8 waves
+// otherwise).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
@@ -251,6 +254,10 @@ medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, 
     launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   else if (Mg <= 4)
     launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (EPI == EPI_LOGITS && Mg > 8 && Mg <= 16)
+    launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (EPI == EPI_LOGITS && Mg > 16)
+    launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   else if (Mg <= 16)
     launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   else
