@@ -446,3 +446,49 @@ def test_verify_pass_lm_head_on_attention_output():
     got = host(z)[0].reshape(B, t.T, V)
     for b in range(B):
         assert rel_err(got[b], z_ref[b]) <= TOL["bf16"], b
+
+
+# ------------------------------------------------------------------ maximum tree
+def test_maximum_tree_end_to_end():
+    # T = MEDUSA_MAX_TREE = 1024 nodes (16 mask words per row), k = 32
+    paths = oracle.greedy_paths(configs.acc_exact, 4, mb.MAX_TREE - 1, 32)
+    ot = oracle.build_tree(paths, 4, 32)
+    assert ot["T"] == mb.MAX_TREE
+    t = mb.Tree(paths, 4, 32).upload()
+    assert np.array_equal(t.mask, ot["mask"])
+    B, V, nh, dh, L, k = 2, 2000, 2, 128, 130, 32
+    g = rng(1024)
+    x = g.standard_normal((4, B, V)).astype(np.float32)
+    root = g.integers(0, V, B).astype(np.int32)
+    idx = torch.empty((4, B, k), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, ot["T"]), dtype=torch.int32, device="cuda")
+    mb.medusa_topk_tree_tokens(t, dev(x), k, dev(root), idx, tok)
+    ri, _ = oracle.topk_per_head(x.astype(np.float64), k)
+    tok_o = oracle.tree_tokens(ot, root, ri)
+    assert np.array_equal(host(tok), tok_o)
+    mk = lambda shape: store(g.standard_normal(shape).astype(np.float32), "bf16")
+    q, kt, vt = mk((B, ot["T"], nh, dh)), mk((B, ot["T"], nh, dh)), mk((B, ot["T"], nh, dh))
+    kc, vc = mk((B, nh, L, dh)), mk((B, nh, L, dh))
+    got = run_attn("bf16", t, q, kt, vt, kc, vc)
+    f = synth.as_f64
+    check_attn("bf16", got, oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot))
+    vl = synth.verification_logits(1024, V, ot["parent"], ot["depth"], ot["rank"], ri, root, configs.acc_float, k)
+    ref = oracle.typical_accept(vl.astype(np.float64), tok_o, ot, 0.09, 0.3, 1.0)
+    check_accept(ot, vl, tok_o, ref, run_accept(t, vl, tok_o, 0.09, 0.3, 1.0))
+    # rejection sampling over the same maximal tree (children up to 32 per node)
+    u_node = g.random((B, ot["T"])).astype(np.float32)
+    u_bonus = g.random(B).astype(np.float32)
+    rr = oracle.rejection_accept(vl.astype(np.float64), x.astype(np.float64), tok_o, ot, 1.0,
+                                 u_node.astype(np.float64), u_bonus.astype(np.float64))
+    o = {n: torch.empty(B, dtype=torch.int32, device="cuda") for n in ("accept_len", "best", "next_tok")}
+    acc = torch.empty((B, ot["depth_max"] + 1), dtype=torch.int32, device="cuda")
+    kp = torch.empty((B, ot["T"]), dtype=torch.float32, device="cuda")
+    mb.rejection_accept(t, dev(vl), dev(x), dev(tok_o.astype(np.int32)), 1.0, dev(u_node), dev(u_bonus),
+                        o["accept_len"], o["best"], o["next_tok"], acc, kp)
+    tested = ~np.isnan(rr["a"])
+    close = np.abs(u_node - np.where(tested, rr["a"], 2.0)) < 1e-4
+    for b in range(B):
+        if close[b].any():
+            continue
+        assert host(o["best"])[b] == rr["best"][b] and host(acc)[b].tolist() == rr["accepted_tok"][b].tolist()
+        assert np.allclose(host(kp)[b][tested[b]], rr["a"][b][tested[b]], rtol=1e-4, atol=1e-6)
