@@ -145,7 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
     int B, int nh, int T, int W, int L, int Lstride, const int32_t *__restrict__ seq_len, float scale_log2,
     int qgroups, int nsplit, int per_split, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const uint64_t *__restrict__ mask,
-    uint16_t *__restrict__ out, float *__restrict__ ws_o, float2 *__restrict__ ws_ml) {
+    const uint32_t *__restrict__ tile_need, uint16_t *__restrict__ out, float *__restrict__ ws_o,
+    float2 *__restrict__ ws_ml) {
   constexpr int DS = DH / 32;  // 32-wide reduction steps over the head dim
   constexpr int DT = DH / 16;  // 16-wide output tiles over the head dim
   __shared__ __attribute__((aligned(16))) uint16_t ks[kKT][DH + kPadK];
@@ -181,14 +182,39 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
   }
 
   // key ranges: prefix slice [c0, c1) of this sequence's Lb cached keys, then
-  // (last slice only) the T tree keys
+  // (last slice only) the tree tiles that hold an ancestor of some query of
+  // the block, in order.  A wave skips the tree tiles none of its queries
+  // needs, and all work of a tile when it has no valid query (it still takes
+  // part in loading the tile).
   const int Lb = seq_len ? min(max(seq_len[b], 0), L) : L;
   const int c0 = split * per_split;
   const int c1 = min(Lb, c0 + per_split);
   const int ncache = c1 > c0 ? (c1 - c0 + kKT - 1) / kKT : 0;
   const bool last = split == nsplit - 1;
-  const int ntree = last ? (T + kKT - 1) / kKT : 0;
+  // (with one query tile per wave the tree has at most 64 tokens: one tile,
+  // needed by every wave, and nothing to skip)
+  constexpr bool kSkip = QT > 1;
+  const int ntree_all = (T + kKT - 1) / kKT;
+  uint32_t need_block = ntree_all >= 32 ? ~0u : (1u << ntree_all) - 1u, need_wave = need_block;
+  bool wave_live = true;
+  if (kSkip) {
+    need_block = need_wave = 0u;
+    const int g0 = qg * 4 * QT, ngroups = (T + 15) / 16;
+    for (int gq = g0; gq < g0 + 4 * QT && gq < ngroups; ++gq) {
+      const uint32_t nb = tile_need[gq];
+      need_block |= nb;
+      if ((gq - g0) / QT == wave) need_wave |= nb;
+    }
+    wave_live = qg * kQB * QT + wave * QT * 16 < T;
+  }
+  const int ntree = last ? (kSkip ? __builtin_popcount(need_block) : ntree_all) : 0;
   const int ntiles = ncache + ntree;
+  auto tree_tile = [&](int i) {  // i-th needed tree tile
+    if (!kSkip) return i;
+    uint32_t m = need_block;
+    for (int j = 0; j < i; ++j) m &= m - 1;
+    return __builtin_ctz(m);
+  };
 
   const long cache_stride = DH;
   const long tree_stride = (long)nh * DH;
@@ -213,16 +239,17 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
     if (tile < ncache)
       load_tile<DH>(r, kc_bh, vc_bh, cache_stride, c0 + tile * kKT, c1);
     else
-      load_tile<DH>(r, kt_bh, vt_bh, tree_stride, (tile - ncache) * kKT, T);
+      load_tile<DH>(r, kt_bh, vt_bh, tree_stride, tree_tile(tile - ncache) * kKT, T);
   };
   auto consume = [&](int tile) {
     const bool is_tree = tile >= ncache;
+    const int tt = is_tree ? tree_tile(tile - ncache) : 0;
+    if (kSkip && (!wave_live || (is_tree && !((need_wave >> tt) & 1u)))) return;
     int kend;
     uint64_t mword[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) mword[qt] = ~0ull;
     if (is_tree) {
-      const int tt = tile - ncache;
       kend = T - tt * kKT;
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt) mword[qt] = qvalid[qt] ? mask[(size_t)tq[qt] * W + tt] : 0ull;
@@ -509,8 +536,8 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
                      t->W, L, pf.Lstride, pf.seq_len, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
-                     static_cast<const uint16_t *>(v_cache), t->d_mask, static_cast<uint16_t *>(out),
-                     ws_o, ws_ml);
+                     static_cast<const uint16_t *>(v_cache), t->d_mask, t->d_tile_need,
+                     static_cast<uint16_t *>(out), ws_o, ws_ml);
   medusa_status s = check_launch("tree_attention");
   if (s != MEDUSA_OK || sp.nsplit == 1) return s;
   const long rows = (long)B * nh * t->T;

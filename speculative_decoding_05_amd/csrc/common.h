@@ -16,12 +16,16 @@ struct medusa_tree {
   std::vector<int32_t> slot;      // node -> index in `internal`, -1 for leaves
   std::vector<int32_t> dstart;    // [depth_max + 2]: nodes of depth d are dstart[d] .. dstart[d+1]-1
   std::vector<uint64_t> mask;     // [T][W]
+  // per group of 16 consecutive nodes: bit w set iff some node of the group
+  // has an ancestor (or is itself) among nodes 64w .. 64w+63
+  std::vector<uint32_t> tile_need;  // [ceil(T/16)]
   // device copy (valid after upload)
   void *d_base = nullptr;
   int device = -1;
   const uint64_t *d_mask = nullptr;
   const int32_t *d_parent = nullptr, *d_depth = nullptr, *d_rank = nullptr;
   const int32_t *d_internal = nullptr, *d_slot = nullptr, *d_dstart = nullptr;
+  const uint32_t *d_tile_need = nullptr;
 };
 
 namespace medusa {

@@ -182,6 +182,10 @@ extern "C" medusa_status medusa_build_tree(const int32_t *ranks, const int32_t *
   t->mask.assign(static_cast<size_t>(t->T) * t->W, 0);
   for (int j = 0; j < t->T; ++j)
     for (int i = j; i != -1; i = t->parent[i]) t->mask[static_cast<size_t>(j) * t->W + i / 64] |= 1ull << (i % 64);
+  t->tile_need.assign((t->T + 15) / 16, 0u);
+  for (int j = 0; j < t->T; ++j)
+    for (int w = 0; w < t->W; ++w)
+      if (t->mask[static_cast<size_t>(j) * t->W + w]) t->tile_need[j / 16] |= 1u << w;
   std::vector<char> has_child(t->T, 0);
   for (int j = 1; j < t->T; ++j) has_child[t->parent[j]] = 1;
   t->slot.assign(t->T, -1);
@@ -237,7 +241,7 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   if (t->d_base) return MEDUSA_OK;
   const size_t T = t->T;
   const size_t mask_b = T * t->W * sizeof(uint64_t);
-  const size_t ints = 4 * T + t->internal.size() + t->dstart.size();
+  const size_t ints = 4 * T + t->internal.size() + t->dstart.size() + t->tile_need.size();
   const size_t bytes = mask_b + ints * sizeof(int32_t);
   std::vector<unsigned char> img(bytes);
   unsigned char *p = img.data();
@@ -250,6 +254,8 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   std::copy(t->slot.begin(), t->slot.end(), q + 3 * T);
   std::copy(t->internal.begin(), t->internal.end(), q + 4 * T);
   std::copy(t->dstart.begin(), t->dstart.end(), q + 4 * T + t->internal.size());
+  std::copy(t->tile_need.begin(), t->tile_need.end(),
+            reinterpret_cast<uint32_t *>(q + 4 * T + t->internal.size() + t->dstart.size()));
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MEDUSA_ERR_HIP, "tree_upload: no HIP device");
   void *d = nullptr;
@@ -271,6 +277,7 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   t->d_slot = di + 3 * T;
   t->d_internal = di + 4 * T;
   t->d_dstart = di + 4 * T + t->internal.size();
+  t->d_tile_need = reinterpret_cast<const uint32_t *>(t->d_dstart + t->dstart.size());
   return MEDUSA_OK;
 }
 
