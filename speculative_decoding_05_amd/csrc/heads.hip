@@ -240,7 +240,8 @@ void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, 
 // stream, that limit these), with two waves splitting the reduction.
 // ResBlock (N = H, few tiles): more waves per block split the reduction so
 // enough loads are in flight (16 waves x 4 k-steps for up to 4 rows, 8 waves
-// otherwise).
+// up to 16 rows, and for 17-32 rows 8 waves of four row tiles sharing each
+// activation fragment).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
@@ -260,6 +261,8 @@ medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, 
     launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   else if (Mg <= 16)
     launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+  else if (H % (32 * 8) == 0)
+    launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   else
     launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
   return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
