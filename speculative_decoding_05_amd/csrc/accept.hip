@@ -196,6 +196,42 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   const int tid = threadIdx.x;
   for (int w = tid; w < MEDUSA_MAX_TREE / 32; w += kScanThreads) s_dec[w] = 0u;
 
+  // 0. issue every load the decisions need now, so that their latency overlaps
+  // the partial merges: each thread owns candidates tid and tid + 512 (T <=
+  // 1024); the candidate's logit under its parent, its token and the first
+  // word of its ancestor mask
+  constexpr int kPer = MEDUSA_MAX_TREE / kScanThreads;
+  int c_tok[kPer], c_par[kPer], c_slot[kPer], c_pslot[kPer], c_depth[kPer];
+  float c_z[kPer];
+  uint64_t c_mask0[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + i * kScanThreads;
+    c_tok[i] = -1;
+    c_par[i] = 0;
+    c_slot[i] = c_pslot[i] = -1;
+    c_depth[i] = 0;
+    c_z[i] = 0.f;
+    c_mask0[i] = 0ull;
+    if (c < T) {
+      c_mask0[i] = mask[(size_t)c * W];
+      c_slot[i] = slot_of[c];
+      c_depth[i] = depth[c];
+      if (c > 0) {
+        c_par[i] = parent[c];
+        c_tok[i] = tree_tok[(size_t)b * T + c];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + i * kScanThreads;
+    if (c > 0 && c < T) {
+      c_pslot[i] = slot_of[c_par[i]];
+      if (!greedy && c_tok[i] >= 0 && c_tok[i] < V) c_z[i] = logits[((size_t)b * T + c_par[i]) * V + c_tok[i]];
+    }
+  }
+
   // 1. per internal row: merge the chunk partials, then the threshold
   for (int sl = tid; sl < n_internal; sl += kScanThreads) {
     const Part *p = part + ((size_t)b * n_internal + sl) * nchunks;
@@ -218,16 +254,18 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   __syncthreads();
 
   // 2. decisions: candidate c against its parent's row
-  for (int c = tid; c < T; c += kScanThreads) {
-    const int sc = slot_of[c];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + i * kScanThreads;
+    if (c >= T) continue;
+    const int sc = c_slot[i];
     if (row_thr) row_thr[(size_t)b * T + c] = sc >= 0 ? s_thr[sc] : NAN;
     if (c == 0) {
       if (cand_p) cand_p[(size_t)b * T] = NAN;
       continue;
     }
-    const int n = parent[c];
-    const int sl = slot_of[n];
-    const int tok = tree_tok[(size_t)b * T + c];
+    const int sl = c_pslot[i];
+    const int tok = c_tok[i];
     float p;
     bool dec;
     if (greedy) {
@@ -237,8 +275,7 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
       p = 0.f;
       dec = false;
     } else {
-      const float zc = logits[((size_t)b * T + n) * V + tok];
-      p = exp2f((zc * inv_tau - s_m[sl]) * kLog2e) / s_S[sl];
+      p = exp2f((c_z[i] * inv_tau - s_m[sl]) * kLog2e) / s_S[sl];
       dec = p > s_thr[sl];
     }
     if (cand_p) cand_p[(size_t)b * T + c] = p;
@@ -248,16 +285,19 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
 
   // 3. accepted iff all ancestors but the root decided yes; deepest, then smallest index
   unsigned int key = 0u;
-  for (int c = tid; c < T; c += kScanThreads) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int c = tid + i * kScanThreads;
+    if (c >= T) continue;
     bool acc = true;
     for (int w = 0; w < W; ++w) {
-      uint64_t anc = mask[(size_t)c * W + w];
+      uint64_t anc = w == 0 ? c_mask0[i] : mask[(size_t)c * W + w];
       if (w == 0) anc &= ~1ull;
       const uint64_t dec = (uint64_t)s_dec[2 * w] | ((uint64_t)s_dec[2 * w + 1] << 32);
       if (anc & ~dec) acc = false;
     }
     if (acc) {
-      const unsigned int k = ((unsigned)depth[c] << 16) | (0xFFFFu - (unsigned)c);
+      const unsigned int k = ((unsigned)c_depth[i] << 16) | (0xFFFFu - (unsigned)c);
       key = k > key ? k : key;
     }
   }
