@@ -127,7 +127,9 @@ medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, i
  *     token id ascending (-0.0 == +0.0); -inf allowed; NaN is not.
  *  logits [R][V] device float;  idx [R][k] device int32 (output);
  *  val    [R][k] device float (output, may be NULL): logits[r][idx].
- *  Limits: 1 <= k <= min(V, MEDUSA_MAX_TOPK).  ws: medusa_topk_workspace bytes.
+ *  Limits: 1 <= k <= min(V, MEDUSA_MAX_TOPK); ceil(V/32768) * k <= 4096.
+ *  ws: medusa_topk_workspace bytes (0 when V <= 32768, then ws may be NULL),
+ *  8-byte aligned; calls that overlap in time must not share it.
  */
 size_t medusa_topk_workspace(int R, int V, int k);
 medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k, const float *logits,
@@ -200,7 +202,7 @@ medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, i
 /* Both of the above in one pass: the per-head top-k of logits [K][B][V]
  * (written to topk_idx [K][B][k]) and the node tokens tree_tok [B][T], each
  * block that finishes a (head, sequence) row writing the tokens of the nodes
- * that row feeds.  ws: medusa_topk_workspace(K*B, V, k) bytes. */
+ * that row feeds.  ws: medusa_topk_workspace(K*B, V, k) bytes, as for medusa_topk. */
 medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B, int K, int V,
                                       int k, const float *logits, const int32_t *root_tok,
                                       int32_t *topk_idx, int32_t *tree_tok, void *ws, size_t ws_bytes);

@@ -5,30 +5,38 @@
 // complement of the index in the low word, so that "larger key" means
 // "larger value, then smaller index" and every row has exactly one answer.
 //
-// One block of 1024 threads holds a chunk of up to 32768 elements of a row in
-// registers.  The block's 64 groups of 16 lanes each find their largest key;
-// the k-th largest of those 64 group maxima, theta, is a lower bound of the
-// chunk's k-th largest key (k distinct keys are >= theta), so every answer is
-// >= theta.  The keys >= theta (typically a few dozen) are appended to LDS and
-// each is ranked exactly by counting the larger candidates; rank r < k goes to
-// output slot r.  Should the candidate set overflow LDS, the block falls back
-// to k rounds of block-wide max extraction.  Rows longer than one chunk write
-// per-chunk candidates that a second kernel merges by the same extraction.
+// A row is cut into slices of NT*PT elements, one NT-thread block each.  In a
+// slice the 64 groups of NT/64 lanes each find their largest 32-bit value
+// image; theta, the largest group maximum that at least k group maxima
+// reach, is a lower bound of the slice's k-th largest value (k distinct
+// elements reach it).  The keys whose image is >= theta (typically a few
+// dozen) are appended to LDS and each is ranked exactly by counting the
+// larger candidates; rank r < k goes to slot r.  Should the candidate set
+// overflow LDS, the block falls back to k rounds of block-wide max
+// extraction.  A row of one slice is finished there; otherwise every slice
+// writes its sorted k keys to the workspace and a second kernel merges each
+// row's lists (a key's rank is the number of larger keys over all lists,
+// found by scanning each list down to its first smaller key).
 #include "common.h"
 
 using namespace medusa;
 
 namespace {
 
-constexpr int kThreads = 256;               // merge kernel
-constexpr int kPerThread = 8;
-constexpr int kMergeMax = kThreads * kPerThread;  // candidates the merge can hold
+constexpr int kCandMax = 1024;   // candidates a slice can rank
+constexpr int kMergeMax = 4096;  // slices * k the merge can hold
+constexpr int kMergeThreads = 256;
 
-__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+__device__ __forceinline__ uint32_t value_image(float v) {
   uint32_t u = __builtin_bit_cast(uint32_t, v);
   if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
-  const uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(mono) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(uint32_t image, uint32_t idx) {
+  return (static_cast<uint64_t>(image) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+  return 0xFFFFFFFFu - static_cast<uint32_t>(key);
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int off) {
@@ -37,39 +45,20 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int off) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
-// k rounds: each round finds the block-wide largest remaining key, removes it
-// from its (unique) owner and appends it to out[] (written by thread 0).
-template <int NT, int E>
-__device__ void block_extract(uint64_t (&keys)[E], int k, uint64_t *out, uint64_t (*s_wave)[NT / 64]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int round = 0; round < k; ++round) {
-    uint64_t best = 0;
-    int bi = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (keys[e] > best) {
-        best = keys[e];
-        bi = e;
-      }
-    uint64_t w = best;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint64_t o = shfl_xor_u64(w, off);
-      w = o > w ? o : w;
-    }
-    uint64_t *buf = s_wave[round & 1];  // alternate buffers: one barrier per round
-    if (lane == 0) buf[wave] = w;
-    __syncthreads();
-    uint64_t g = buf[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) g = buf[i] > g ? buf[i] : g;
-    if (g != 0 && best == g) {
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (e == bi) keys[e] = 0;
-    }
-    if (threadIdx.x == 0) out[round] = g;
+// max over aligned groups of G lanes (G = 4 or 16), result in every lane
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  uint32_t o = dpp<kDppXor1>(v);
+  v = o > v ? o : v;
+  o = dpp<kDppXor2>(v);
+  v = o > v ? o : v;
+  if (G == 16) {
+    o = dpp<kDppHalfMirror>(v);
+    v = o > v ? o : v;
+    o = dpp<kDppMirror>(v);
+    v = o > v ? o : v;
   }
+  return v;
 }
 
 // Optional tree-token scatter: the block that finishes row (head, b) writes the
@@ -87,87 +76,92 @@ __device__ __forceinline__ void scatter_tokens(const TokenScatter &ts, int row, 
   if (head + 1 > ts.depth_max) return;
   const int j0 = ts.dstart[head + 1], j1 = ts.dstart[head + 2];
   for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x)
-    ts.tree_tok[(size_t)b * ts.T + j] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(s_out[ts.rank[j]]));
+    ts.tree_tok[(size_t)b * ts.T + j] = static_cast<int32_t>(key_index(s_out[ts.rank[j]]));
   if (head == 0 && threadIdx.x == 0) ts.tree_tok[(size_t)b * ts.T] = ts.root[b];
 }
 
-constexpr int kFThreads = 1024;
-constexpr int kFE = 32;
-constexpr int kFChunk = kFThreads * kFE;  // 32768 elements per block
-constexpr int kCandMax = 1024;
+// idx/val/scatter of a finished row from its sorted keys
+__device__ __forceinline__ void emit_row(const float *z, int row, int k, const uint64_t *s_out, int32_t *idx,
+                                         float *val, const TokenScatter &ts) {
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const uint32_t id = key_index(s_out[j]);
+    idx[(size_t)row * k + j] = static_cast<int32_t>(id);
+    if (val) val[(size_t)row * k + j] = z[id];
+  }
+  scatter_tokens(ts, row, s_out);
+}
 
-__global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict__ logits, int V, int k,
-                                                        int nchunks, int32_t *__restrict__ idx,
-                                                        float *__restrict__ val,
-                                                        uint64_t *__restrict__ part, TokenScatter ts) {
-  __shared__ uint64_t s_gmax[kFThreads / 16];
+template <int NT, int PT>
+__global__ __launch_bounds__(NT) void topk_slices(const float *__restrict__ logits, int V, int k, int nslices,
+                                                  int32_t *__restrict__ idx, float *__restrict__ val,
+                                                  uint64_t *__restrict__ part, TokenScatter ts) {
+  constexpr int G = NT / 64;  // lanes per group; 64 groups
+  __shared__ uint32_t s_gmax[64];
   __shared__ uint64_t s_cand[kCandMax];
   __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
-  __shared__ uint64_t s_wave[2][kFThreads / 64];
-  __shared__ uint64_t s_theta;
+  __shared__ uint64_t s_wave[2][NT / 64];
+  __shared__ uint32_t s_theta;
   __shared__ int s_cnt;
-  const int tid = threadIdx.x;
-  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int slice = blockIdx.x, row = blockIdx.y;
   const float *z = logits + (size_t)row * V;
-  const int base = chunk * kFChunk;
-  // values stay in registers as floats; keys are rebuilt from (value, index).
-  // Element e of this thread is index base + (e/4)*4096 + 4*tid + e%4, read
-  // as float4 when the row allows it.
-  float v[kFE];
-  const bool vec = (V % 4) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0;
+  const int base = slice * NT * PT;
+  // element e of this thread is index base + (e/4)*4*NT + 4*tid + e%4; every
+  // load is issued unconditionally (clamped into the row), indices >= V are
+  // masked afterwards
+  auto index_of = [&](int e) { return base + (e >> 2) * 4 * NT + 4 * tid + (e & 3); };
+  uint32_t img[PT];
+  if ((V % 4) == 0 && (reinterpret_cast<uintptr_t>(z) & 15) == 0) {
 #pragma unroll
-  for (int g = 0; g < kFE / 4; ++g) {
-    const int i0 = base + g * 4 * kFThreads + 4 * tid;
-    if (vec && i0 + 3 < V) {
+    for (int g = 0; g < PT / 4; ++g) {
+      const int i0 = min(index_of(4 * g), V - 4);
       const float4 f = *reinterpret_cast<const float4 *>(z + i0);
-      v[4 * g] = f.x;
-      v[4 * g + 1] = f.y;
-      v[4 * g + 2] = f.z;
-      v[4 * g + 3] = f.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 * g + j] = i0 + j < V ? z[i0 + j] : 0.f;
+      img[4 * g] = value_image(f.x);
+      img[4 * g + 1] = value_image(f.y);
+      img[4 * g + 2] = value_image(f.z);
+      img[4 * g + 3] = value_image(f.w);
     }
-  }
-  auto index_of = [&](int e) { return base + (e >> 2) * 4 * kFThreads + 4 * tid + (e & 3); };
-  auto key_of = [&](int e) -> uint64_t {
-    const int i = index_of(e);
-    return i < V ? make_key(v[e], static_cast<uint32_t>(i)) : 0ull;
-  };
-  uint64_t m = 0;
+  } else {
 #pragma unroll
-  for (int e = 0; e < kFE; ++e) {
-    const uint64_t key = key_of(e);
-    m = key > m ? key : m;
+    for (int e = 0; e < PT; ++e) img[e] = value_image(z[min(index_of(e), V - 1)]);
   }
-  m = row_max_u64(m);  // DPP steps within each 16-lane group
-  if ((tid & 15) == 0) s_gmax[tid >> 4] = m;
+  // images of indices >= V become 0, at or below every valid image
+  uint32_t m = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    if (index_of(e) >= V) img[e] = 0u;
+    m = img[e] > m ? img[e] : m;
+  }
+  m = group_max<G>(m);
+  if ((tid & (G - 1)) == 0) s_gmax[tid / G] = m;
   if (tid < MEDUSA_MAX_TOPK) s_out[tid] = 0ull;
-  if (tid == 0) {
-    s_theta = 1ull;  // fewer than k non-empty groups: every valid key is a candidate
-    s_cnt = 0;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  if (wave == 0) {
+    // theta = largest group maximum reached by at least k group maxima (a
+    // group maximum of 0 is at most every valid image, so theta = 0 admits
+    // every valid element)
+    const uint32_t g = s_gmax[lane];
+    int reach = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) reach += s_gmax[j] >= g ? 1 : 0;
+    const uint32_t t = wave_max_u32(reach >= k ? g : 0u);
+    if (lane == 0) s_theta = t;
   }
   __syncthreads();
-  if (tid < kFThreads / 16) {
-    const uint64_t v = s_gmax[tid];
-    int rank = 0;
-    for (int j = 0; j < kFThreads / 16; ++j) rank += s_gmax[j] > v ? 1 : 0;
-    if (v != 0ull && rank == k - 1) s_theta = v;
-  }
-  __syncthreads();
-  const uint64_t theta = s_theta;
+  const uint32_t theta = s_theta;
 #pragma unroll
-  for (int e = 0; e < kFE; ++e) {
-    const uint64_t key = key_of(e);
-    if (key >= theta) {
+  for (int e = 0; e < PT; ++e) {
+    const int i = index_of(e);
+    if (i < V && img[e] >= theta) {
       const int p = atomicAdd(&s_cnt, 1);
-      if (p < kCandMax) s_cand[p] = key;
+      if (p < kCandMax) s_cand[p] = make_key(img[e], static_cast<uint32_t>(i));
     }
   }
   __syncthreads();
   const int C = s_cnt;
   if (C <= kCandMax) {
-    for (int i = tid; i < C; i += kFThreads) {
+    for (int i = tid; i < C; i += NT) {
       const uint64_t key = s_cand[i];
       int rank = 0;
       for (int j = 0; j < C; ++j) rank += s_cand[j] > key ? 1 : 0;
@@ -175,16 +169,17 @@ __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict_
     }
   } else {
     // overflow (rare: e.g. massive ties): k rounds of block-wide max; the
-    // values are re-read from memory so the fast path keeps its registers
-    const int wave = tid >> 6, lane = tid & 63;
+    // values are re-read from memory so that the common path keeps its
+    // registers (keys hoisted out of this loop would spill)
     uint32_t taken = 0u;
     for (int round = 0; round < k; ++round) {
-      uint64_t best = 0;
+      uint64_t best = 0ull;
       int bi = 0;
 #pragma unroll 1
-      for (int e = 0; e < kFE; ++e) {
+      for (int e = 0; e < PT; ++e) {
         const int i = index_of(e);
-        const uint64_t key = ((taken >> e) & 1u) || i >= V ? 0ull : make_key(z[i], static_cast<uint32_t>(i));
+        const uint64_t key =
+            ((taken >> e) & 1u) || i >= V ? 0ull : make_key(value_image(z[i]), static_cast<uint32_t>(i));
         if (key > best) {
           best = key;
           bi = e;
@@ -196,54 +191,48 @@ __global__ __launch_bounds__(kFThreads) void topk_chunk(const float *__restrict_
         const uint64_t o = shfl_xor_u64(w, off);
         w = o > w ? o : w;
       }
-      uint64_t *buf = s_wave[round & 1];
+      uint64_t *buf = s_wave[round & 1];  // alternate buffers: one barrier per round
       if (lane == 0) buf[wave] = w;
       __syncthreads();
       uint64_t g = buf[0];
 #pragma unroll
-      for (int i = 1; i < kFThreads / 64; ++i) g = buf[i] > g ? buf[i] : g;
+      for (int i = 1; i < NT / 64; ++i) g = buf[i] > g ? buf[i] : g;
       if (g != 0ull && best == g) taken |= 1u << bi;
       if (tid == 0) s_out[round] = g;
     }
   }
   __syncthreads();
-  for (int j = tid; j < k; j += kFThreads) {
-    const uint64_t key = s_out[j];
-    if (nchunks == 1) {
-      const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(key);
-      idx[(size_t)row * k + j] = static_cast<int32_t>(id);
-      if (val) val[(size_t)row * k + j] = z[id];
-    } else {
-      part[((size_t)row * nchunks + chunk) * k + j] = key;
-    }
+  if (nslices == 1) {
+    emit_row(z, row, k, s_out, idx, val, ts);
+  } else {
+    // this slice's sorted list (zeros pad a slice of fewer than k elements)
+    for (int j = tid; j < k; j += NT) part[((size_t)row * nslices + slice) * k + j] = s_out[j];
   }
-  if (nchunks == 1) scatter_tokens(ts, row, s_out);
 }
 
-__global__ __launch_bounds__(kThreads) void topk_stage2(const float *__restrict__ logits, int V,
-                                                        int k, int nchunks,
-                                                        const uint64_t *__restrict__ part,
-                                                        int32_t *__restrict__ idx,
-                                                        float *__restrict__ val, TokenScatter ts) {
-  __shared__ uint64_t s_wave[2][kThreads / 64];
+// One block per row: merge the slices' sorted lists.
+__global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *__restrict__ logits, int V, int k,
+                                                            int nslices, const uint64_t *__restrict__ part,
+                                                            int32_t *__restrict__ idx, float *__restrict__ val,
+                                                            TokenScatter ts) {
+  __shared__ uint64_t s_all[kMergeMax];
   __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
-  const int row = blockIdx.x;
-  const int n = nchunks * k;
-  const uint64_t *p = part + (size_t)row * n;
-  uint64_t keys[kPerThread];
-#pragma unroll
-  for (int e = 0; e < kPerThread; ++e) {
-    const int i = e * kThreads + threadIdx.x;
-    keys[e] = i < n ? p[i] : 0ull;
-  }
-  block_extract<kThreads, kPerThread>(keys, k, s_out, s_wave);
+  const int row = blockIdx.x, n = nslices * k;
+  const uint64_t *rp = part + (size_t)row * n;
+  for (int c = threadIdx.x; c < n; c += kMergeThreads) s_all[c] = rp[c];
   __syncthreads();
-  for (int j = threadIdx.x; j < k; j += kThreads) {
-    const uint32_t id = 0xFFFFFFFFu - static_cast<uint32_t>(s_out[j]);
-    idx[(size_t)row * k + j] = static_cast<int32_t>(id);
-    if (val) val[(size_t)row * k + j] = logits[(size_t)row * V + id];
+  for (int c = threadIdx.x; c < n; c += kMergeThreads) {
+    const uint64_t x = s_all[c];
+    if (x == 0ull) continue;
+    int rank = 0;
+    for (int s = 0; s < nslices && rank < k; ++s) {
+      const uint64_t *lst = s_all + s * k;
+      for (int j = 0; j < k && lst[j] > x; ++j) ++rank;
+    }
+    if (rank < k) s_out[rank] = x;
   }
-  scatter_tokens(ts, row, s_out);
+  __syncthreads();
+  emit_row(logits + (size_t)row * V, row, k, s_out, idx, val, ts);
 }
 
 __global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restrict__ depth,
@@ -255,14 +244,22 @@ __global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restric
   tok[i] = j == 0 ? root[b] : topk_idx[((size_t)(depth[j] - 1) * B + b) * k + rank[j]];
 }
 
-inline int chunks_for(int V) { return (V + kFChunk - 1) / kFChunk; }
+// Slice shape: 1024 threads x 32 elements = 32768, a whole 32000-token row in
+// one block with no merge.  (Slices of 256 x 16 with a merge kernel measured
+// slower at 4 and 64 rows of 32000: the second launch costs more than the
+// wider block.)
+constexpr int kNT = 1024, kPT = 32;
+constexpr int kSlice = kNT * kPT;
+inline int slices_for(int V) { return (V + kSlice - 1) / kSlice; }
 
 }  // namespace
 
+// Workspace of rows of several slices: their sorted lists [R][slices][k] of
+// 64-bit keys.
 extern "C" size_t medusa_topk_workspace(int R, int V, int k) {
   if (R < 1 || V < 1 || k < 1) return 0;
-  const int nchunks = chunks_for(V);
-  return nchunks > 1 ? (size_t)R * nchunks * k * sizeof(uint64_t) : 0;
+  const int ns = slices_for(V);
+  return ns > 1 ? (size_t)R * ns * k * sizeof(uint64_t) : 0;
 }
 
 static medusa_status topk_launch(const char *who, hipStream_t st, int R, int V, int k, const float *logits,
@@ -271,18 +268,20 @@ static medusa_status topk_launch(const char *who, hipStream_t st, int R, int V, 
   if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "%s: k=%d outside [1, V=%d]", who, k, V);
   if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: k=%d > %d", who, k, MEDUSA_MAX_TOPK);
   if (!logits || !idx) return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
-  const int nchunks = chunks_for(V);
-  if ((long)nchunks * k > kMergeMax)
+  const int ns = slices_for(V);
+  if ((long)ns * k > kMergeMax)
     return fail(MEDUSA_ERR_UNSUPPORTED, "%s: V=%d with k=%d exceeds the merge capacity", who, V, k);
   const size_t need = medusa_topk_workspace(R, V, k);
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu", who, ws_bytes, need);
   if (need > 0 && !ws) return fail(MEDUSA_ERR_ARG, "%s: NULL workspace", who);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 7u))
+    return fail(MEDUSA_ERR_ARG, "%s: workspace must be 8-byte aligned", who);
   if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: R=%d > 65535", who, R);
   uint64_t *part = static_cast<uint64_t *>(ws);
-  hipLaunchKernelGGL(topk_chunk, dim3(nchunks, R), dim3(kFThreads), 0, st, logits, V, k, nchunks, idx, val, part, ts);
+  hipLaunchKernelGGL((topk_slices<kNT, kPT>), dim3(ns, R), dim3(kNT), 0, st, logits, V, k, ns, idx, val, part, ts);
   medusa_status s = check_launch(who);
-  if (s != MEDUSA_OK || nchunks == 1) return s;
-  hipLaunchKernelGGL(topk_stage2, dim3(R), dim3(kThreads), 0, st, logits, V, k, nchunks, part, idx, val, ts);
+  if (s != MEDUSA_OK || ns == 1) return s;
+  hipLaunchKernelGGL(topk_merge, dim3(R), dim3(kMergeThreads), 0, st, logits, V, k, ns, part, idx, val, ts);
   return check_launch(who);
 }
 
