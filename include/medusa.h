@@ -102,24 +102,35 @@ medusa_status medusa_heads(medusa_stream_t stream, medusa_dtype dt, int K, int M
                            float *logits);
 
 /* Packed weights (bf16).  The same projections with W1 / W2 stored once,
- * ahead of decoding, in the matrix-core fragment order: for head k, row tile t
- * (rows 16t..16t+15) and reduction step s (columns 32s..32s+31),
- *   Wp[k][t][s][l][e] = W[k][16t + l % 16][32s + 8 (l / 16) + e],
- * l < 64, e < 8, rows >= N zero.  Each fragment is one contiguous 1 KiB block,
- * so the hot calls stream the weights linearly.
- *  medusa_packed_weight_bytes: size of Wp for W [K][N][H] (0 if H % 32 != 0).
+ * ahead of decoding, in the matrix-core fragment order.  A fragment is the
+ * 16 x 32 block of head k at row tile t (rows 16t..16t+15) and reduction step
+ * s (columns 32s..32s+31), one contiguous 1 KiB block in lane order:
+ *   frag[l][e] = W[k][16t + l % 16][32s + 8 (l / 16) + e],  l < 64, e < 8
+ * (rows >= N zero).  The fragments of `group` consecutive row tiles (group =
+ * 1, 2, 4 or 8) are interleaved step by step: within head k, fragment (t, s)
+ * is number ((t / group) * (H / 32) + s) * group + t % group, and each head
+ * holds ceil(N / 128) * 8 row tiles.  group = 1 keeps every tile's steps
+ * contiguous and streams fastest to calls of up to 8 rows; group = 8 streams
+ * fastest to 9 and more rows (measured on MI355X);
+ * medusa_pack_group_for_rows(M) returns that choice.  The *_packed calls take
+ * the group Wp was packed with.
+ *  medusa_packed_weight_bytes: size of Wp for W [K][N][H] (0 if H % 32 != 0),
+ *                       the same for every group.
  *  medusa_pack_weights: W [K][N][H] bf16 (device) -> Wp (device, caller-owned,
- *                       medusa_packed_weight_bytes bytes); needs H % 128 == 0.
+ *                       medusa_packed_weight_bytes bytes); needs H % 128 == 0;
+ *                       ERR_ARG for a group outside {1, 2, 4, 8}.
  *  *_packed: as the calls above with dt = MEDUSA_BF16 and W1p = pack(W1)
  *            (N = H), W2p = pack(W2) (N = V). */
 size_t medusa_packed_weight_bytes(int K, int N, int H);
-medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H, const void *W, void *Wp);
-medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H, const void *h,
-                                          const void *W1p, void *r);
-medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V,
+int medusa_pack_group_for_rows(int M);
+medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H, int group, const void *W,
+                                  void *Wp);
+medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H, int group,
+                                          const void *h, const void *W1p, void *r);
+medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                        const void *r, const void *W2p, float *logits);
-medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, const void *h,
-                                  const void *W1p, const void *W2p, void *r, float *logits);
+medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
+                                  const void *h, const void *W1p, const void *W2p, void *r, float *logits);
 
 /* ------------------------------------------------------------------------- */
 /* (2) Top-k of every row.  Tutorial page, sections "候选生成" and "每头 Top-K":

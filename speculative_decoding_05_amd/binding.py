@@ -39,10 +39,11 @@ SIGNATURES = {
     "medusa_head_vocab": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_heads": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
     "medusa_packed_weight_bytes": (_sz, [_i, _i, _i]),
-    "medusa_pack_weights": (_i, [_p, _i, _i, _i, _p, _p]),
-    "medusa_head_resblock_packed": (_i, [_p, _i, _i, _i, _p, _p, _p]),
-    "medusa_head_vocab_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
-    "medusa_heads_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
+    "medusa_pack_group_for_rows": (_i, [_i]),
+    "medusa_pack_weights": (_i, [_p, _i, _i, _i, _i, _p, _p]),
+    "medusa_head_resblock_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
+    "medusa_head_vocab_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "medusa_heads_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
     "medusa_topk_workspace": (_sz, [_i, _i, _i]),
     "medusa_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_dense_paths": (_i, [_i, _i, _i, _ip, _ip, ctypes.POINTER(_i)]),
@@ -145,36 +146,45 @@ def medusa_heads(h, W1, W2, r, logits):
     return logits
 
 
-class PackedWeights:
-    """bf16 head weights [K][N][H] reordered once into the matrix-core fragment order."""
+def medusa_pack_group_for_rows(M):
+    return lib.medusa_pack_group_for_rows(M)
 
-    def __init__(self, W):
+
+class PackedWeights:
+    """bf16 head weights [K][N][H] reordered once into the matrix-core fragment
+    order, row tiles interleaved in groups of `group` (1, 2, 4 or 8)."""
+
+    def __init__(self, W, group=1):
         torch = _torch()
         _dev(W)
         if W.dtype != torch.bfloat16:
             raise TypeError("packed weights are bf16")
         self.K, self.N, self.H = W.shape
+        self.group = int(group)
         nbytes = lib.medusa_packed_weight_bytes(self.K, self.N, self.H)
         self.data = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=W.device)
-        check(lib.medusa_pack_weights(_stream(), self.K, self.N, self.H, _ptr(W), _ptr(self.data)))
+        check(lib.medusa_pack_weights(_stream(), self.K, self.N, self.H, self.group, _ptr(W), _ptr(self.data)))
 
 
 def medusa_head_resblock_packed(h, W1p, r):
     _dev(h, r)
-    check(lib.medusa_head_resblock_packed(_stream(), W1p.K, h.shape[0], W1p.H, _ptr(h), _ptr(W1p.data), _ptr(r)))
+    check(lib.medusa_head_resblock_packed(_stream(), W1p.K, h.shape[0], W1p.H, W1p.group, _ptr(h), _ptr(W1p.data),
+                                          _ptr(r)))
     return r
 
 
 def medusa_head_vocab_packed(r, W2p, logits):
     _dev(r, logits)
-    check(lib.medusa_head_vocab_packed(_stream(), W2p.K, r.shape[1], W2p.H, W2p.N, _ptr(r), _ptr(W2p.data),
-                                       _ptr(logits)))
+    check(lib.medusa_head_vocab_packed(_stream(), W2p.K, r.shape[1], W2p.H, W2p.N, W2p.group, _ptr(r),
+                                       _ptr(W2p.data), _ptr(logits)))
     return logits
 
 
 def medusa_heads_packed(h, W1p, W2p, r, logits):
     _dev(h, r, logits)
-    check(lib.medusa_heads_packed(_stream(), W2p.K, h.shape[0], W2p.H, W2p.N, _ptr(h), _ptr(W1p.data),
+    if W1p.group != W2p.group:
+        raise ValueError("W1p and W2p must share one packing group")
+    check(lib.medusa_heads_packed(_stream(), W2p.K, h.shape[0], W2p.H, W2p.N, W2p.group, _ptr(h), _ptr(W1p.data),
                                   _ptr(W2p.data), _ptr(r), _ptr(logits)))
     return logits
 

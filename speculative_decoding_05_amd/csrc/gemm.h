@@ -7,13 +7,31 @@ namespace medusa {
 
 enum { kEpiResblock = 0, kEpiLogits = 1 };
 
+// Packed weight layout (medusa_pack_weights).  A fragment is one 16 x 32
+// block of W (16 output rows, 32 reduction elements) stored as 1 KiB in MFMA
+// lane order: lane l holds row l%16, elements 8(l/16)..+7.  Fragments are
+// grouped by G = 2^lgG consecutive row tiles (G = 1, 2, 4 or 8): within a
+// head, fragment (tile t, step s) is number ((t/G)*S + s)*G + t%G, S = H/32,
+// so the G tiles of a group lie side by side at every step.  G = 1 keeps each
+// tile's steps contiguous (fastest to stream one tile per wave, few rows);
+// G = 8 gives 8 KiB runs to waves that own 8 tiles (9-32 rows).  Row tiles
+// are padded with zeros to a multiple of 8 whatever G is.
+constexpr int kPackGroupMax = 8;
+__host__ __device__ inline int packed_tiles(int N) {
+  return (N + 16 * kPackGroupMax - 1) / (16 * kPackGroupMax) * kPackGroupMax;
+}
+__host__ __device__ inline size_t packed_fragment(int t, int s, int S, int lgG) {
+  return ((((size_t)(t >> lgG)) * S + s) << lgG) + (t & ((1 << lgG) - 1));
+}
+
 // out[head][m][n] = sum_i W[head][n][i] * X[head*xhs + m*H + i], m < M, n < N:
 //   kEpiLogits:   of[head][m][n] = the sum (fp32)
 //   kEpiResblock: ob[head][m][n] = bf16(resid[m][n] + SiLU(sum))   (N == H)
 // W row-major [K][N][H] or packed (medusa_pack_weights).  H % 64 == 0.
+// lgG: log2 of the packed layout's tile group (packed weights only).
 template <int EPI, bool PACKED>
 medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
-                                  int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of);
+                                  int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of);
 
 // From this many rows the tiled kernel replaces the weight-streaming one (one
 // group of MEDUSA_MAX_HEADS_M rows streams the weights once; past that the

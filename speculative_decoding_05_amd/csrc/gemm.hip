@@ -62,7 +62,7 @@ struct TileShape {
 template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM, int BK, int MINW>
 __global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
-    int H, int M, int GM, const uint16_t *__restrict__ resid, uint16_t *__restrict__ out_bf16,
+    int H, int M, int GM, int lgG, const uint16_t *__restrict__ resid, uint16_t *__restrict__ out_bf16,
     float *__restrict__ out_f32) {
   using S = TileShape<BN, BM, WGN, WGM, BK>;
   constexpr int kLdk = S::kLdk;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
   // launcher checks that a head's operands span less than 4 GiB; rows past the
   // end re-read the last row) and LDS destinations, affine in the slot j.
   const int NTt = (N + 15) / 16, Ssteps = H / 32;
-  const char *wbase = reinterpret_cast<const char *>(W) + (PACKED ? (size_t)head * NTt * Ssteps * 1024
+  const char *wbase = reinterpret_cast<const char *>(W) + (PACKED ? (size_t)head * packed_tiles(N) * Ssteps * 1024
                                                                    : (size_t)head * N * H * 2);
   const char *xbase = reinterpret_cast<const char *>(X) + (size_t)head * x_head_stride * 2;
   uint32_t woff[S::WCH], xoff[S::XCH];
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
       // slot c: lane c%64 of fragment F = c/64: row tile F/SPT, k-step F%SPT
       const int F = c >> 6;
       const int t = min(n0 / 16 + F / S::SPT, NTt - 1);
-      woff[j] = ((uint32_t)(t * Ssteps + F % S::SPT) * 64u + (uint32_t)(c & 63)) * 16u;
+      woff[j] = ((uint32_t)packed_fragment(t, F % S::SPT, Ssteps, lgG) * 64u + (uint32_t)(c & 63)) * 16u;
     } else {
       // slot c: row c/CPR, columns 8*(c%CPR)..+7 (each row's k-tile in CPR lanes)
       const int n = min(n0 + c / S::CPR, N - 1);
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
                            : (tid / S::CPR) * kLdk + (tid % S::CPR) * 8;
   const int xdst0 = BN * kLdk + (tid / S::CPR) * kLdk + (tid % S::CPR) * 8;
   constexpr int kXdstStep = (S::kThreads / S::CPR) * kLdk;
-  const uint32_t w_step = PACKED ? S::SPT * 1024u : BK * 2u;   // bytes per k-tile
+  const uint32_t w_step = PACKED ? (S::SPT * 1024u) << lgG : BK * 2u;   // bytes per k-tile
 
   // two register sets: tile j is loaded into set j % 2
   u32x4_t wreg[2][S::WCH], xreg[2][S::XCH];
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * WGN * WGM, MINW) void head_gemm_tiled(
 
 template <int EPI, bool PACKED, int BN, int BM, int WGN, int WGM, int BK, int MINW>
 medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N,
-                           int H, int M, int GM, const uint16_t *resid, uint16_t *ob, float *of) {
+                           int H, int M, int GM, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
   using S = TileShape<BN, BM, WGN, WGM, BK>;
   if (H % (2 * BK) != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% %d != 0 (H=%d)", 2 * BK, H);
   auto kern = head_gemm_tiled<EPI, PACKED, BN, BM, WGN, WGM, BK, MINW>;
@@ -243,7 +243,7 @@ medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X,
   const long blocks = (long)K * ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
   if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(S::kThreads), S::kLdsBytes, st, W, X, xhs, N, H, M,
-                     GM, resid, ob, of);
+                     GM, lgG, resid, ob, of);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab (tiled)" : "medusa_head_resblock (tiled)");
 }
 
@@ -253,24 +253,24 @@ namespace medusa {
 
 template <int EPI, bool PACKED>
 medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
-                                  int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  const size_t w_head = PACKED ? (size_t)((N + 15) / 16) * (H / 32) * 1024 : (size_t)N * H * 2;
+                                  int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+  const size_t w_head = PACKED ? (size_t)packed_tiles(N) * (H / 32) * 1024 : (size_t)N * H * 2;
   if (w_head >= (1ull << 32) || (size_t)M * H * 2 >= (1ull << 32))
     return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
-  return launch_tiled<EPI, PACKED, 256, 256, 2, 4, 64, 1>(st, W, X, xhs, K, N, H, M, 8, resid, ob, of);
+  return launch_tiled<EPI, PACKED, 256, 256, 2, 4, 64, 1>(st, W, X, xhs, K, N, H, M, 8, lgG, resid, ob, of);
 }
 
 template medusa_status head_gemm_many_rows<kEpiResblock, false>(hipStream_t, const uint16_t *, const uint16_t *,
-                                                                long, int, int, int, int, const uint16_t *,
+                                                                long, int, int, int, int, int, const uint16_t *,
                                                                 uint16_t *, float *);
 template medusa_status head_gemm_many_rows<kEpiResblock, true>(hipStream_t, const uint16_t *, const uint16_t *,
-                                                               long, int, int, int, int, const uint16_t *,
+                                                               long, int, int, int, int, int, const uint16_t *,
                                                                uint16_t *, float *);
 template medusa_status head_gemm_many_rows<kEpiLogits, false>(hipStream_t, const uint16_t *, const uint16_t *,
-                                                              long, int, int, int, int, const uint16_t *,
+                                                              long, int, int, int, int, int, const uint16_t *,
                                                               uint16_t *, float *);
 template medusa_status head_gemm_many_rows<kEpiLogits, true>(hipStream_t, const uint16_t *, const uint16_t *,
-                                                             long, int, int, int, int, const uint16_t *,
+                                                             long, int, int, int, int, int, const uint16_t *,
                                                              uint16_t *, float *);
 
 }  // namespace medusa

@@ -10,12 +10,12 @@
 // the epilogue (SiLU + residual + bf16 rounding, or fp32 store) is fused.
 //
 // Two weight layouts are accepted.  Row-major [K][N][H]: every load
-// instruction touches 16 rows x 64 bytes.  Packed (medusa_pack_weights): each
-// 16x32 A fragment is stored as one contiguous 1 KiB block in lane order, so
-// every load instruction of a wave reads 1 KiB of consecutive bytes and each
-// wave streams one contiguous region -- the layout reaches the HBM streaming
-// rate that the row-major pattern loses to scattered row segments.  Weights are
-// read with non-temporal loads so the small activation block stays in L2.
+// instruction touches 16 rows x 64 bytes.  Packed (medusa_pack_weights, layout
+// in gemm.h): each 16x32 A fragment is one contiguous 1 KiB block in lane
+// order, so every load instruction of a wave reads 1 KiB of consecutive bytes
+// -- the layout reaches the HBM streaming rate that the row-major pattern
+// loses to scattered row segments.  Weights are read with non-temporal loads
+// so the small activation block stays in L2.
 #include "common.h"
 #include "gemm.h"
 
@@ -43,7 +43,7 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
 template <int R, int C, int EPI, bool PACKED, int U, int NW>
 __global__ __launch_bounds__(64 * NW) void head_gemm_bf16(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
-    int H, int M_total, int m0, int Mg, int tiles_per_head, const uint16_t *__restrict__ resid,
+    int H, int M_total, int m0, int Mg, int tiles_per_head, int lgG, const uint16_t *__restrict__ resid,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
   __shared__ float red[NW][16 * C][16 * R + 1];
   const int head = blockIdx.x / tiles_per_head;
@@ -59,15 +59,17 @@ __global__ __launch_bounds__(64 * NW) void head_gemm_bf16(
   const uint16_t *arow[R];
   int a_step;
   if (PACKED) {
-    // fragment (tile t, step s) at ((head*NT + t)*S + s)*512, lane l at +8*l
+    // fragment f of a head at f*512 elements, lane l at +8*l; consecutive
+    // steps of one tile are G = 2^lgG fragments apart
     const int S = H / 32, NT = (N + 15) / 16;
     const int t0 = n0 / 16;
+    const uint16_t *Wh_p = W + (size_t)head * packed_tiles(N) * S * 512 + lane * 8;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int t = t0 + r < NT ? t0 + r : NT - 1;  // ragged tail: valid tile, result discarded
-      arow[r] = W + (((size_t)head * NT + t) * S + wave * (kspan / 32)) * 512 + lane * 8;
+      arow[r] = Wh_p + packed_fragment(t, wave * (kspan / 32), S, lgG) * 512;
     }
-    a_step = 512;
+    a_step = 512 << lgG;
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -203,23 +205,27 @@ __global__ __launch_bounds__(256) void head_gemm_f32(const float *__restrict__ W
 }
 
 
-// Packed layout: Wp[k][t][s][l][e] = W[k][16t + l%16][32s + 8(l/16) + e]
-// (t < ceil(N/16), s < H/32, l < 64, e < 8; rows >= N are zero).
+// Packed layout (gemm.h), G = 2^lgG:
+// Wp[k][g][s][j][l][e] = W[k][16(G g + j) + l%16][32s + 8(l/16) + e]
+// (g < packed_tiles(N)/G, s < H/32, j < G, l < 64, e < 8; rows >= N are zero).
 // One thread moves one 16-byte lane slice.
 __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__restrict__ W,
                                                            uint16_t *__restrict__ Wp, int K, int N,
-                                                           int H) {
-  const int S = H / 32, NT = (N + 15) / 16;
-  const size_t total = (size_t)K * NT * S * 64;
+                                                           int H, int lgG) {
+  const int G = 1 << lgG;
+  const int S = H / 32, NG = packed_tiles(N) >> lgG;
+  const size_t total = (size_t)K * NG * S * G * 64;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const int l = (int)(i % 64);
   size_t f = i / 64;
+  const int j = (int)(f & (G - 1));
+  f >>= lgG;
   const int s = (int)(f % S);
   f /= S;
-  const int t = (int)(f % NT);
-  const int k = (int)(f / NT);
-  const int n = t * 16 + (l & 15);
+  const int g = (int)(f % NG);
+  const int k = (int)(f / NG);
+  const int n = ((g << lgG) + j) * 16 + (l & 15);
   u32x4_t v = {0u, 0u, 0u, 0u};
   if (n < N) v = *reinterpret_cast<const u32x4_t *>(W + ((size_t)k * N + n) * H + s * 32 + (l >> 4) * 8);
   *reinterpret_cast<u32x4_t *>(Wp + i * 8) = v;
@@ -227,10 +233,10 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__res
 
 template <int R, int C, int EPI, bool PACKED, int U, int NW>
 void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
-                int m0, int Mg, const uint16_t *resid, uint16_t *ob, float *of) {
+                int m0, int Mg, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
   const int tiles = (N + 16 * R - 1) / (16 * R);
   hipLaunchKernelGGL((head_gemm_bf16<R, C, EPI, PACKED, U, NW>), dim3(tiles * K), dim3(64 * NW), 0, st, W, X, xhs,
-                     N, H, M, m0, Mg, tiles, resid, ob, of);
+                     N, H, M, m0, Mg, tiles, lgG, resid, ob, of);
 }
 
 // Tiling by shape (measured on MI355X).  Vocabulary projection (N = V, many
@@ -244,27 +250,27 @@ void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, 
 // activation fragment).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
-                          int N, int H, int M, const uint16_t *resid, uint16_t *ob, float *of) {
-  if (M >= kManyRows) return head_gemm_many_rows<EPI, PACKED>(st, W, X, xhs, K, N, H, M, resid, ob, of);
+                          int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+  if (M >= kManyRows) return head_gemm_many_rows<EPI, PACKED>(st, W, X, xhs, K, N, H, M, lgG, resid, ob, of);
   const int m0 = 0, Mg = M;   // one group: the weights are streamed once
   if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
-    launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
-    launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
-    launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4)
-    launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_LOGITS && Mg > 8 && Mg <= 16)
-    launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_LOGITS && Mg > 16)
-    launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 16)
-    launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (H % (32 * 8) == 0)
-    launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else
-    launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, resid, ob, of);
+    launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
 }
 
@@ -299,7 +305,7 @@ extern "C" medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dty
   hipStream_t st = as_stream(stream);
   if (dt == MEDUSA_BF16)
     return launch_bf16<EPI_RESBLOCK, false>(st, static_cast<const uint16_t *>(W1), static_cast<const uint16_t *>(h),
-                                     0, K, H, H, M, static_cast<const uint16_t *>(h),
+                                     0, K, H, H, M, 0, static_cast<const uint16_t *>(h),
                                      static_cast<uint16_t *>(r), nullptr);
   return launch_f32<EPI_RESBLOCK>(st, static_cast<const float *>(W1), static_cast<const float *>(h), 0,
                                   K, H, H, M, static_cast<const float *>(h), static_cast<float *>(r));
@@ -318,7 +324,7 @@ extern "C" medusa_status medusa_head_vocab(medusa_stream_t stream, medusa_dtype 
   const long xhs = (long)M * H;
   if (dt == MEDUSA_BF16)
     return launch_bf16<EPI_LOGITS, false>(st, static_cast<const uint16_t *>(W2), static_cast<const uint16_t *>(r),
-                                   xhs, K, V, H, M, nullptr, nullptr, logits);
+                                   xhs, K, V, H, M, 0, nullptr, nullptr, logits);
   return launch_f32<EPI_LOGITS>(st, static_cast<const float *>(W2), static_cast<const float *>(r), xhs,
                                 K, V, H, M, nullptr, logits);
 }
@@ -341,47 +347,66 @@ extern "C" medusa_status medusa_heads(medusa_stream_t stream, medusa_dtype dt, i
 // packed-weight entry points (bf16)
 extern "C" size_t medusa_packed_weight_bytes(int K, int N, int H) {
   if (K < 1 || N < 1 || H < 32 || H % 32 != 0) return 0;
-  return (size_t)K * ((N + 15) / 16) * (H / 32) * 512 * sizeof(uint16_t);
+  return (size_t)K * packed_tiles(N) * (H / 32) * 512 * sizeof(uint16_t);
 }
 
-extern "C" medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H,
+// log2 of a packed layout's tile group, or -1 if the group is not 1, 2, 4 or 8
+static int group_log2(int group) {
+  switch (group) {
+    case 1: return 0;
+    case 2: return 1;
+    case 4: return 2;
+    case 8: return 3;
+  }
+  return -1;
+}
+
+extern "C" int medusa_pack_group_for_rows(int M) { return M <= 8 ? 1 : kPackGroupMax; }
+
+extern "C" medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H, int group,
                                              const void *W, void *Wp) {
   if (K < 1 || N < 1 || H < 1) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: K=%d N=%d H=%d", K, N, H);
+  const int lgG = group_log2(group);
+  if (lgG < 0) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: group=%d not in {1, 2, 4, 8}", group);
   if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_pack_weights: needs H %% 128 == 0 (H=%d)", H);
   if (!W || !Wp) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: NULL pointer");
   if (!aligned16(W) || !aligned16(Wp)) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: pointers must be 16-byte aligned");
   const size_t lanes = medusa_packed_weight_bytes(K, N, H) / 16;
   hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, as_stream(stream),
-                     static_cast<const uint16_t *>(W), static_cast<uint16_t *>(Wp), K, N, H);
+                     static_cast<const uint16_t *>(W), static_cast<uint16_t *>(Wp), K, N, H, lgG);
   return check_launch("medusa_pack_weights");
 }
 
-extern "C" medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H,
+extern "C" medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H, int group,
                                                      const void *h, const void *W1p, void *r) {
   medusa_status s = check_common("medusa_head_resblock_packed", MEDUSA_BF16, K, M, H);
   if (s != MEDUSA_OK) return s;
+  const int lgG = group_log2(group);
+  if (lgG < 0) return fail(MEDUSA_ERR_ARG, "medusa_head_resblock_packed: group=%d not in {1, 2, 4, 8}", group);
   if (!h || !W1p || !r) return fail(MEDUSA_ERR_ARG, "medusa_head_resblock_packed: NULL pointer");
   if (!aligned16(h) || !aligned16(W1p) || !aligned16(r))
     return fail(MEDUSA_ERR_ARG, "medusa_head_resblock_packed: pointers must be 16-byte aligned");
   return launch_bf16<EPI_RESBLOCK, true>(as_stream(stream), static_cast<const uint16_t *>(W1p),
-                                         static_cast<const uint16_t *>(h), 0, K, H, H, M,
+                                         static_cast<const uint16_t *>(h), 0, K, H, H, M, lgG,
                                          static_cast<const uint16_t *>(h), static_cast<uint16_t *>(r), nullptr);
 }
 
-extern "C" medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V,
+extern "C" medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                                   const void *r, const void *W2p, float *logits) {
   medusa_status s = check_common("medusa_head_vocab_packed", MEDUSA_BF16, K, M, H);
   if (s != MEDUSA_OK) return s;
+  const int lgG = group_log2(group);
+  if (lgG < 0) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: group=%d not in {1, 2, 4, 8}", group);
   if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: V=%d", V);
   if (!r || !W2p || !logits) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: NULL pointer");
   if (!aligned16(r) || !aligned16(W2p) || !aligned16(logits))
     return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed: pointers must be 16-byte aligned");
   return launch_bf16<EPI_LOGITS, true>(as_stream(stream), static_cast<const uint16_t *>(W2p),
-                                       static_cast<const uint16_t *>(r), (long)M * H, K, V, H, M, nullptr,
+                                       static_cast<const uint16_t *>(r), (long)M * H, K, V, H, M, lgG, nullptr,
                                        nullptr, logits);
 }
 
-extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V,
+extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                              const void *h, const void *W1p, const void *W2p, void *r,
                                              float *logits) {
   medusa_status s = check_common("medusa_heads_packed", MEDUSA_BF16, K, M, H);
@@ -390,7 +415,7 @@ extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int 
   if (!h || !W1p || !W2p || !r || !logits) return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: NULL pointer");
   if (!aligned16(h) || !aligned16(W1p) || !aligned16(W2p) || !aligned16(r) || !aligned16(logits))
     return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: pointers must be 16-byte aligned");
-  s = medusa_head_resblock_packed(stream, K, M, H, h, W1p, r);
+  s = medusa_head_resblock_packed(stream, K, M, H, group, h, W1p, r);
   if (s != MEDUSA_OK) return s;
-  return medusa_head_vocab_packed(stream, K, M, H, V, r, W2p, logits);
+  return medusa_head_vocab_packed(stream, K, M, H, V, group, r, W2p, logits);
 }

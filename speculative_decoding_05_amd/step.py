@@ -54,8 +54,9 @@ class Step:
             self.W1 = to_device(host["W1"], dev)
             self.W2 = to_device(host["W2"], dev)
             if self.packed:  # one-time reorder into the matrix-core fragment order
-                self.W1p = mb.PackedWeights(self.W1)
-                self.W2p = mb.PackedWeights(self.W2)
+                group = mb.medusa_pack_group_for_rows(B)   # the heads see B rows per step
+                self.W1p = mb.PackedWeights(self.W1, group)
+                self.W2p = mb.PackedWeights(self.W2, group)
                 torch.cuda.synchronize()
                 del self.W1, self.W2
         self.root = to_device(host["root_tok"].astype(np.int32), dev)
@@ -144,7 +145,7 @@ class VerifyPass:
             W_lm = to_device(W_lm).reshape(1, V, H)
         else:
             W_lm = (torch.randn((1, V, H), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
-        self.W_lm = mb.PackedWeights(W_lm)
+        self.W_lm = mb.PackedWeights(W_lm, mb.medusa_pack_group_for_rows(M))
         torch.cuda.synchronize()
         del W_lm
         self.r = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")

@@ -25,14 +25,14 @@ def head_inputs(dtype, K, M, H, V, seed):
     return h, W1, W2
 
 
-def run_heads(dtype, h, W1, W2, packed=False):
+def run_heads(dtype, h, W1, W2, packed=False, group=1):
     K, V, H = W2.shape
     M = h.shape[0]
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
     r = torch.full((K, M, H), float("nan"), dtype=td, device="cuda")
     logits = torch.full((K, M, V), float("nan"), dtype=torch.float32, device="cuda")
     if packed:
-        mb.medusa_heads_packed(dev(h), mb.PackedWeights(dev(W1)), mb.PackedWeights(dev(W2)), r, logits)
+        mb.medusa_heads_packed(dev(h), mb.PackedWeights(dev(W1), group), mb.PackedWeights(dev(W2), group), r, logits)
     else:
         mb.medusa_heads(dev(h), dev(W1), dev(W2), r, logits)
     return host(r), host(logits)
@@ -100,25 +100,31 @@ def test_zero_w1_many_rows_bitwise():
     assert rel_err(lg_g[0], ref) <= TOL["bf16"]
 
 
-def test_packed_equals_row_major_bitwise():
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_packed_equals_row_major_bitwise(group):
     # the packed layout only changes where the weights sit, not the arithmetic
-    for K, M, H, V in [(4, 1, 512, 1000), (2, 20, 256, 333), (2, 300, 256, 1001)]:
+    for K, M, H, V in [(4, 1, 512, 1000), (3, 12, 256, 1500), (2, 20, 256, 333), (2, 300, 256, 1001)]:
         h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=M)
         a = run_heads("bf16", h, W1, W2, packed=False)
-        b = run_heads("bf16", h, W1, W2, packed=True)
+        b = run_heads("bf16", h, W1, W2, packed=True, group=group)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def test_pack_layout():
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_pack_layout(group):
     K, N, H = 2, 37, 128
     W = store(rng(5).standard_normal((K, N, H)).astype(np.float32), "bf16")
-    Wp = host(mb.PackedWeights(dev(W)).data.view(torch.int16)).astype(np.int64) & 0xFFFF
-    NT, S = (N + 15) // 16, H // 32
-    Wp = Wp.reshape(K, NT, S, 64, 8)
-    for k, t, s_, l in [(0, 0, 0, 0), (1, 2, 3, 63), (1, 1, 2, 17), (0, 2, 1, 40)]:
+    Wp = host(mb.PackedWeights(dev(W), group).data.view(torch.int16)).astype(np.int64) & 0xFFFF
+    # row tiles of 16 (padded with zero tiles to a multiple of 8) in groups of
+    # `group`; within a group the tiles' fragments of one reduction step lie
+    # side by side
+    NTp, S = (N + 127) // 128 * 8, H // 32
+    assert Wp.size == K * NTp * S * 64 * 8
+    Wp = Wp.reshape(K, NTp // group, S, group, 64, 8)
+    for k, t, s_, l in [(0, 0, 0, 0), (1, 2, 3, 63), (1, 1, 2, 17), (0, 2, 1, 40), (1, 7, 0, 5), (0, 3, 3, 31)]:
         n = 16 * t + l % 16
         want = W[k, n, 32 * s_ + 8 * (l // 16):32 * s_ + 8 * (l // 16) + 8] if n < N else np.zeros(8)
-        assert Wp[k, t, s_, l].tolist() == np.asarray(want, np.int64).tolist()
+        assert Wp[k, t // group, s_, t % group, l].tolist() == np.asarray(want, np.int64).tolist()
 
 
 @pytest.mark.parametrize("M", [6, 70])

@@ -129,8 +129,11 @@ def test_device_calls_validate_before_launch():
     assert mb.lib.medusa_topk(None, 2, 10, 11, fake, fake, None, fake, 1 << 20) == mb.ERR_ARG
     assert mb.lib.medusa_topk(None, 2, 100, 65, fake, fake, None, fake, 1 << 20) == mb.ERR_UNSUPPORTED
     assert mb.lib.medusa_topk(None, 2, 40000, 4, fake, fake, None, fake, 8) == mb.ERR_WORKSPACE
-    assert mb.lib.medusa_pack_weights(None, 2, 10, 100, fake, fake) == mb.ERR_UNSUPPORTED
-    assert mb.lib.medusa_heads_packed(None, 4, 1, 256, 0, fake, fake, fake, fake, fake) == mb.ERR_ARG
+    assert mb.lib.medusa_pack_weights(None, 2, 10, 100, 1, fake, fake) == mb.ERR_UNSUPPORTED
+    assert mb.lib.medusa_pack_weights(None, 2, 10, 128, 3, fake, fake) == mb.ERR_ARG      # group not a power of 2
+    assert mb.lib.medusa_head_vocab_packed(None, 2, 1, 128, 10, 16, fake, fake, fake) == mb.ERR_ARG
+    assert mb.lib.medusa_heads_packed(None, 4, 1, 256, 0, 1, fake, fake, fake, fake, fake) == mb.ERR_ARG
+    assert [mb.medusa_pack_group_for_rows(m) for m in (1, 8, 9, 32, 1000)] == [1, 1, 8, 8, 8]
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 100, 50, fake, fake, fake, fake, fake) == mb.ERR_UNSUPPORTED
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 50, fake, None, fake, fake, fake) == mb.ERR_ARG
     assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 50, P(0x1008), fake, fake, fake, fake) == mb.ERR_ARG
