@@ -61,15 +61,25 @@ def stage_flops(cfg, tree):
 
 
 PROFILE = os.path.join(ROOT, "profiles", "head_vocab_vicuna7b_b1.md")
-KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_05_amd", "csrc", "heads.hip")
+# sources the vocabulary-projection kernel is compiled from (kernel, packed
+# layout helpers, shared device helpers); the recorded digest covers all three
+KERNEL_SRCS = [os.path.join(ROOT, "speculative_decoding_05_amd", "csrc", f)
+               for f in ("heads.hip", "gemm.h", "common.h")]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def counted_traffic(workload):
     """HBM bytes per launch of the vocabulary projection from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the plain-copy
     calibration recorded there); None if there is none for this workload or
-    the kernel source changed since the counters were taken."""
-    import hashlib
+    the kernel sources changed since the counters were taken."""
     try:
         lines = open(PROFILE).read().splitlines()
     except OSError:
@@ -80,8 +90,7 @@ def counted_traffic(workload):
             rec = json.loads(ln[len("traffic: "):])
     if not rec or rec.get("workload") != workload:
         return None
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if sha != rec.get("source_sha256"):
+    if kernel_sources_sha256() != rec.get("source_sha256"):
         return None
     return rec["bytes_per_launch"]
 
