@@ -405,8 +405,8 @@ def main():
                     help="bracket the vocabulary projection with events on every n-th timed step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus}: this build measures one GPU only; the verify tree-step "
-              "has no multi-GPU path (sequences shard with no exchange).", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus}: only one GPU is measured; the verify tree-step has no "
+              "multi-GPU path (sequences would shard across GPUs with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
