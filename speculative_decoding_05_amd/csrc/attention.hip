@@ -43,6 +43,7 @@ constexpr int kPadV = 16;      // row padding (bf16) of the V tile: 8 rows of a 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMinKeysPerSplit = 256;
 constexpr int kSplitTargetBlocks = 128;
+constexpr int kMergeUnroll = 8;       // slices the merge loads in one round
 constexpr long kCUs = 256;     // compute units of the device
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -393,20 +394,47 @@ __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T
   const long nrows = (long)B * nh * T;
   if (row >= nrows) return;
   const size_t stride = (size_t)nrows;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[s * stride + row].x);
-  const float Mu = M == -INFINITY ? 0.f : M;
   float l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nsplit; ++s) {
-    const float2 ml = ws_ml[s * stride + row];
-    const float w = exp2f(ml.x - Mu);
-    l += w * ml.y;
-    const float4 p = *reinterpret_cast<const float4 *>(ws_o + (s * stride + row) * DH + c);
-    o.x += w * p.x;
-    o.y += w * p.y;
-    o.z += w * p.z;
-    o.w += w * p.w;
+  if (nsplit <= kMergeUnroll) {
+    // every slice's (m, l) and partial O are loaded in one round
+    float2 ml[kMergeUnroll];
+    float4 po[kMergeUnroll];
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s) {
+      const int sl = s < nsplit ? s : nsplit - 1;
+      ml[s] = ws_ml[sl * stride + row];
+      po[s] = *reinterpret_cast<const float4 *>(ws_o + (sl * stride + row) * DH + c);
+    }
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s)
+      if (s < nsplit) M = fmaxf(M, ml[s].x);
+    const float Mu = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int s = 0; s < kMergeUnroll; ++s)
+      if (s < nsplit) {
+        const float w = exp2f(ml[s].x - Mu);
+        l += w * ml[s].y;
+        o.x += w * po[s].x;
+        o.y += w * po[s].y;
+        o.z += w * po[s].z;
+        o.w += w * po[s].w;
+      }
+  } else {
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[s * stride + row].x);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    for (int s = 0; s < nsplit; ++s) {
+      const float2 ml = ws_ml[s * stride + row];
+      const float w = exp2f(ml.x - Mu);
+      l += w * ml.y;
+      const float4 p = *reinterpret_cast<const float4 *>(ws_o + (s * stride + row) * DH + c);
+      o.x += w * p.x;
+      o.y += w * p.y;
+      o.z += w * p.z;
+      o.w += w * p.w;
+    }
   }
   const float inv = 1.f / l;
   // row = (b*nh + h)*T + t  ->  out[b][t][h][:]
