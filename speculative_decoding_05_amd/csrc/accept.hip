@@ -28,6 +28,7 @@ constexpr int kVec = 4;                        // float4 per thread: 4096-wide c
                                                // faster than 16384-wide ones at every shape)
 constexpr int kScanThreads = 512;              // scan
 constexpr int kBatch = 8;                      // independent loads issued together
+constexpr int kLeafBatch = 16;                 // float4 loads per thread for a leaf row's argmax
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Part {  // 32 bytes
@@ -326,21 +327,19 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   const float *z = logits + ((size_t)b * T + best) * V;
   Stat st = empty_stat();
   if ((V % 4) == 0) {
+    // a 32768-wide row in one round of loads (16 float4 per thread, issued
+    // unconditionally at clamped indices; indices past the row are skipped)
     const int V4 = V / 4;
-    for (int base = tid; base < V4; base += kScanThreads * kBatch) {
-      f32x4_t v[kBatch];
+    for (int base = tid; base < V4; base += kScanThreads * kLeafBatch) {
+      f32x4_t v[kLeafBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = base + u * kScanThreads;
-        v[u] = i < V4 ? *reinterpret_cast<const f32x4_t *>(z + 4 * i)
-                      : f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      }
+      for (int u = 0; u < kLeafBatch; ++u)
+        v[u] = *reinterpret_cast<const f32x4_t *>(z + 4 * min(base + u * kScanThreads, V4 - 1));
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u)
+      for (int u = 0; u < kLeafBatch; ++u)
+        if (base + u * kScanThreads < V4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * (base + u * kScanThreads) + j;
-          if (i < V) arg_better(st.av, st.ai, v[u][j], i);
+          for (int j = 0; j < 4; ++j) arg_better(st.av, st.ai, v[u][j], 4 * (base + u * kScanThreads) + j);
         }
     }
   } else {
