@@ -151,6 +151,8 @@ def test_heads_rows_and_heads_independent_bitwise(M):
     (2, 50000, 10, "normal"), (2, 70001, 64, "normal"),          # several chunks + merge
     (3, 32000, 10, "overflow"), (2, 32000, 64, "overflow"),      # candidate overflow fallback
     (2, 32768, 10, "ties"), (64, 32000, 4, "normal"),
+    (2, 128256, 64, "normal"), (3, 131077, 10, "ties"),          # 4 and 5 slices merged
+    (2, 4, 4, "normal"), (2, 1, 1, "normal"), (4, 7, 3, "zeros"),  # rows shorter than one load
 ])
 def test_topk_bit_exact(R, V, k, kind):
     say("topk", R, V, k, kind)
