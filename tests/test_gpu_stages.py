@@ -103,7 +103,8 @@ def test_zero_w1_many_rows_bitwise():
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_packed_equals_row_major_bitwise(group):
     # the packed layout only changes where the weights sit, not the arithmetic
-    for K, M, H, V in [(4, 1, 512, 1000), (3, 12, 256, 1500), (2, 20, 256, 333), (2, 300, 256, 1001)]:
+    for K, M, H, V in [(4, 1, 512, 1000), (3, 12, 256, 1500), (2, 20, 256, 333), (2, 48, 256, 700),
+                       (2, 300, 256, 1001)]:
         h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=M)
         a = run_heads("bf16", h, W1, W2, packed=False)
         b = run_heads("bf16", h, W1, W2, packed=True, group=group)
@@ -127,7 +128,7 @@ def test_pack_layout(group):
         assert Wp[k, t // group, s_, t % group, l].tolist() == np.asarray(want, np.int64).tolist()
 
 
-@pytest.mark.parametrize("M", [6, 70])
+@pytest.mark.parametrize("M", [6, 40, 70])
 def test_heads_rows_and_heads_independent_bitwise(M):
     K, H, V = 3, 256, 300
     h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=9)
