@@ -260,7 +260,10 @@ medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint1
   // up to 64 rows the work is weight-streaming bound: 64-row activation
   // tiles, 128-row weight tiles and two blocks per CU (measured at 64 rows,
   // 7B shape: ResBlock 120 -> 38 us, vocabulary 287 -> 191 us, LM head
-  // 157 -> 48 us against the 256 x 256 tile)
+  // 157 -> 48 us against the 256 x 256 tile); 64-row weight tiles when the
+  // 128-row ones would give at most half a block per CU (ResBlock: 38 -> 30 us)
+  if (M <= 64 && (long)K * ((N + 127) / 128) <= 128)
+    return launch_tiled<EPI, PACKED, 64, 64, 2, 2, 64, 2>(st, W, X, xhs, K, N, H, M, 8, lgG, resid, ob, of);
   if (M <= 64) return launch_tiled<EPI, PACKED, 128, 64, 2, 2, 64, 2>(st, W, X, xhs, K, N, H, M, 8, lgG, resid, ob, of);
   return launch_tiled<EPI, PACKED, 256, 256, 2, 4, 64, 1>(st, W, X, xhs, K, N, H, M, 8, lgG, resid, ob, of);
 }
