@@ -132,6 +132,28 @@ medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int
 medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                   const void *h, const void *W1p, const void *W2p, void *r, float *logits);
 
+/* Workspace variants of the packed calls, for many rows (the verify-pass
+ * shape M = B*T, and the backbone's LM head over the tree nodes).  Same
+ * arguments and results as medusa_head_resblock_packed /
+ * medusa_head_vocab_packed (bit-identical: the same products, summed in the
+ * same order), plus a caller-owned device workspace.  With M >= 65 the
+ * activations (h, resp. r) are first copied into the workspace in the
+ * fragment order of the packed weights (row tile of 16 rows x 32 columns as
+ * one 1 KiB block in lane order), so that both operands of the block-tiled
+ * matrix-core contraction stream as whole fragments; with M < 65 the calls
+ * above run and ws is not touched (it may then be NULL).
+ *  medusa_head_workspace(K, M, H): bytes of ws, K * ceil(M/16) * (H/32) KiB
+ *                       for M >= 65 and H % 128 == 0, else 0.
+ *  ws: device, 16-byte aligned, >= medusa_head_workspace(K, M, H) bytes
+ *      (ERR_WORKSPACE if smaller); its contents on return are unspecified.
+ *  Limits as the packed calls, and each head's packed activations < 4 GiB. */
+size_t medusa_head_workspace(int K, int M, int H);
+medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, int K, int M, int H, int group,
+                                             const void *h, const void *W1p, void *r, void *ws, size_t ws_bytes);
+medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
+                                          const void *r, const void *W2p, float *logits, void *ws,
+                                          size_t ws_bytes);
+
 /* ------------------------------------------------------------------------- */
 /* (2) Top-k of every row.  Tutorial page, sections "候选生成" and "每头 Top-K":
  *     each head contributes its top-k tokens.  Order: value descending, then

@@ -44,6 +44,9 @@ SIGNATURES = {
     "medusa_head_resblock_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_head_vocab_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_heads_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
+    "medusa_head_workspace": (_sz, [_i, _i, _i]),
+    "medusa_head_resblock_packed_ws": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz]),
+    "medusa_head_vocab_packed_ws": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_topk_workspace": (_sz, [_i, _i, _i]),
     "medusa_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_dense_paths": (_i, [_i, _i, _i, _ip, _ip, ctypes.POINTER(_i)]),
@@ -186,6 +189,32 @@ def medusa_heads_packed(h, W1p, W2p, r, logits):
         raise ValueError("W1p and W2p must share one packing group")
     check(lib.medusa_heads_packed(_stream(), W2p.K, h.shape[0], W2p.H, W2p.N, W2p.group, _ptr(h), _ptr(W1p.data),
                                   _ptr(W2p.data), _ptr(r), _ptr(logits)))
+    return logits
+
+
+def medusa_head_workspace(K, M, H):
+    return lib.medusa_head_workspace(K, M, H)
+
+
+def medusa_head_resblock_packed_ws(h, W1p, r, ws=None):
+    _dev(h, r)
+    M = h.shape[0]
+    if ws is None:
+        ws = workspace(lib.medusa_head_workspace(W1p.K, M, W1p.H), h.device)
+    _dev(ws)
+    check(lib.medusa_head_resblock_packed_ws(_stream(), W1p.K, M, W1p.H, W1p.group, _ptr(h), _ptr(W1p.data),
+                                             _ptr(r), _ptr(ws), ws.numel() * ws.element_size()))
+    return r
+
+
+def medusa_head_vocab_packed_ws(r, W2p, logits, ws=None):
+    _dev(r, logits)
+    M = r.shape[1]
+    if ws is None:
+        ws = workspace(lib.medusa_head_workspace(W2p.K, M, W2p.H), r.device)
+    _dev(ws)
+    check(lib.medusa_head_vocab_packed_ws(_stream(), W2p.K, M, W2p.H, W2p.N, W2p.group, _ptr(r), _ptr(W2p.data),
+                                          _ptr(logits), _ptr(ws), ws.numel() * ws.element_size()))
     return logits
 
 

@@ -33,6 +33,21 @@ template <int EPI, bool PACKED>
 medusa_status head_gemm_many_rows(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                                   int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of);
 
+// Activations in fragment order (the packed-weight layout with G = 1, applied to
+// [K][M][H] rows): K * ceil(M/16) * (H/32) KiB; 0 for invalid sizes.
+size_t packed_rows_bytes(int K, int M, int H);
+// X [K][M][H] (head stride xhs elements) -> Xp (packed_rows_bytes(K, M, H) bytes)
+medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int M, int H, uint16_t *Xp);
+// As head_gemm_many_rows with packed weights, the activations given in fragment
+// order: x_heads = 1 shares one packed [M][H] among all heads (the ResBlock's
+// h), x_heads = K gives each head its own.  H % 128 == 0.
+template <int EPI>
+medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
+                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of);
+// From this many rows the workspace variants of the packed calls run
+// head_gemm_fragments (below it the weight-streaming and 64-row kernels).
+constexpr int kFragmentRows = 65;
+
 // From this many rows the tiled kernel replaces the weight-streaming one (one
 // group of MEDUSA_MAX_HEADS_M rows streams the weights once; past that the
 // tiled kernel re-uses each weight tile across up to 256 rows).

@@ -247,7 +247,267 @@ medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X,
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab (tiled)" : "medusa_head_resblock (tiled)");
 }
 
+// ---------------------------------------------------------------------------
+// Fragment-fed variant for many rows (used when both operands are stored in
+// matrix-core fragment order: the packed weights, and activations packed by
+// pack_rows_kernel into a caller's workspace).
+//
+// Why a second kernel: with the activations row-major, every activation
+// fragment is a gather of 16 rows x 64 bytes, and the load path (texture
+// addresser) is the busiest unit; stored as 1 KiB fragments, both operands
+// are single contiguous wave loads.  Those go straight from global memory into
+// LDS (global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane,
+// i.e. a fragment stays in lane order), so there are no staging registers, no
+// padding and no LDS bank conflicts, and a fragment is read back with one
+// ds_read_b128 per lane.
+//
+// Block tile 256 (weight rows n) x 256 (activation rows m), one 32-deep
+// reduction step per stage, four stages (4 x 32 KiB of LDS) with the loads for
+// step s+3 issued while step s is computed.  Four waves, one per SIMD, each
+// owning a 128 x 128 sub-tile: 64 v_mfma_f32_16x16x32_bf16 per step from 8 A
+// (weight) and 8 B (activation) fragments, which halves the LDS bytes per
+// matrix-core op against 128 x 64 sub-tiles.  The 256 accumulator registers per
+// lane live in AGPRs; the compiler's own MFMA selection there uses the untied
+// form and permutes all of them every trip, so the MFMA is issued through a
+// tied inline-asm operand ("+a").  The fragments of step s+1 are read into the
+// second register set between the MFMAs of step s (one read per four MFMAs, A
+// fragments first, whose last readers are the first MFMAs of the step before),
+// and the eight loads per wave and step sit between the MFMA groups, so the
+// matrix core starts right after each step's barrier.
+//
+// Hazard padding the compiler cannot add around inline asm: s_nop blocks after
+// the accumulators are zeroed and before they are read back.
+//
+// Ordering per step s (vmcnt counts this wave's loads, all into LDS):
+//   wait vmcnt(8)  -> this wave's loads of step s+1 are in LDS (only step s+2's
+//                     eight may be outstanding); lgkmcnt(0) -> step s's fragments
+//                     are in registers
+//   s_barrier      -> every wave's loads of step s+1 are in LDS, and every wave
+//                     has finished reading step s-1's stage, which the loads of
+//                     step s+3 now overwrite ((s+3) % 4 == (s-1) % 4)
+// The stages are four separate __shared__ arrays and the loop is unrolled by
+// four, so the compiler's wait insertion can tell them apart (one shared
+// array would make it wait for every outstanding load before each read).
+
+typedef uint32_t u32x4_frag_t __attribute__((ext_vector_type(4)));
+constexpr int kFragStageVec = 2048;                 // 32 fragments of 1 KiB, in 16-byte vectors
+__shared__ u32x4_frag_t frag_stage0[kFragStageVec];
+__shared__ u32x4_frag_t frag_stage1[kFragStageVec];
+__shared__ u32x4_frag_t frag_stage2[kFragStageVec];
+__shared__ u32x4_frag_t frag_stage3[kFragStageVec];
+
+template <int B>
+__device__ __forceinline__ u32x4_frag_t *frag_stage() {
+  if (B == 0) return frag_stage0;
+  if (B == 1) return frag_stage1;
+  if (B == 2) return frag_stage2;
+  return frag_stage3;
+}
+
+// s_waitcnt with vmcnt = vm and lgkmcnt = lgkm (gfx9 encoding; expcnt left at its maximum)
+#define MEDUSA_WAITCNT(vm, lgkm) \
+  __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | ((((vm) >> 4) & 3) << 14) | (7 << 4) | (((lgkm) & 0xF) << 8))
+
+__device__ __forceinline__ void mfma_tied(f32x4_t &c, u32x4_t a, u32x4_t b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void dma16(const char *g, u32x4_frag_t *l) {
+  // address-space casts (C-style: reinterpret_cast cannot change the address space)
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
+                                   (void __attribute__((address_space(3))) *)l, 16, 0, 0);
+}
+
+// Activations [K][M][H] (head stride xhs elements) -> fragment order
+// [K][ceil(M/16)][H/32][64 lanes][8]: lane l of fragment (row tile t, step s)
+// holds row 16t + l % 16, columns 32s + 8(l / 16) .. + 7; rows >= M are zero.
+__global__ void pack_rows_kernel(const uint16_t *__restrict__ X, long xhs, int K, int M, int H,
+                                 uint16_t *__restrict__ Xp) {
+  const int S = H / 32, MT = (M + 15) / 16;
+  const size_t total = (size_t)K * MT * S * 64;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int l = (int)(i & 63);
+  size_t f = i >> 6;
+  const int s = (int)(f % S);
+  f /= S;
+  const int t = (int)(f % MT);
+  const int k = (int)(f / MT);
+  const int m = t * 16 + (l & 15);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (m < M) v = *reinterpret_cast<const u32x4_t *>(X + (size_t)k * xhs + (size_t)m * H + s * 32 + (l >> 4) * 8);
+  *reinterpret_cast<u32x4_t *>(Xp + i * 8) = v;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void head_gemm_frag(const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp,
+                                                          int x_heads, int N, int H, int M, int GM, int lgG,
+                                                          const uint16_t *__restrict__ resid,
+                                                          uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
+  constexpr int BN = 256, BM = 256, kAhead = 3;
+  const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+  const int per_head = tiles_n * tiles_m;
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int head = id / per_head;
+  id -= head * per_head;
+  const int span = GM * tiles_n;
+  const int grp = id / span;
+  const int mfirst = grp * GM;
+  const int gm = min(GM, tiles_m - mfirst);
+  const int rem = id - grp * span;
+  const int m0 = (mfirst + rem % gm) * BM, n0 = (rem / gm) * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS addresses stay scalar
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int S = H / 32, NT = packed_tiles(N), MT = (M + 15) / 16;
+  const char *wbase = reinterpret_cast<const char *>(Wp) + (size_t)head * NT * S * 1024;
+  const char *xbase = reinterpret_cast<const char *>(Xp) + (x_heads > 1 ? (size_t)head * MT * S * 1024 : 0);
+  // this wave loads weight fragments (row tiles) 4w..4w+3 and activation fragments 4w..4w+3 of
+  // the block at every step; tiles past the end re-read the last one (their results are not stored)
+  uint32_t woff[4], xoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = min(n0 / 16 + 4 * wave + j, NT - 1);
+    woff[j] = (uint32_t)packed_fragment(t, 0, S, lgG) * 1024u + lane * 16u;
+    const int mt = min(m0 / 16 + 4 * wave + j, MT - 1);
+    xoff[j] = (uint32_t)mt * S * 1024u + lane * 16u;
+  }
+  const uint32_t wstep = 1024u << lgG;   // bytes between one row tile's consecutive steps
+  auto dma = [&](int s, u32x4_frag_t *stg, int q) {
+    if (q < 4)
+      dma16(wbase + woff[q] + (uint32_t)s * wstep, stg + (4 * wave + q) * 64);
+    else
+      dma16(xbase + xoff[q - 4] + (uint32_t)s * 1024u, stg + (16 + 4 * wave + q - 4) * 64);
+  };
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int g = 0; g < 8; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t fr[2][16];   // [register set][8 weight fragments, 8 activation fragments]
+  const int aoff = wn * 8 * 64 + lane, boff = (16 + wm * 8) * 64 + lane;
+  const int nsteps = S;   // a multiple of 4 (H % 128 == 0)
+
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma(0, frag_stage<0>(), q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma(min(1, nsteps - 1), frag_stage<1>(), q);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma(min(2, nsteps - 1), frag_stage<2>(), q);
+  MEDUSA_WAITCNT(16, 15);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) fr[0][i] = frag_stage<0>()[i < 8 ? aoff + i * 64 : boff + (i - 8) * 64];
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto body = [&](int s, int set, const u32x4_frag_t *nxt, u32x4_frag_t *dst) {
+    MEDUSA_WAITCNT(8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int sd = min(s + kAhead, nsteps - 1);   // past the end: re-load the last step into a stage never read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      fr[set ^ 1][i] = nxt[i < 8 ? aoff + i * 64 : boff + (i - 8) * 64];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = i * 4 + j, f = q >> 3, g = q & 7;
+        mfma_tied(acc[f][g], fr[set][f], fr[set][8 + g]);
+      }
+      if (i & 1) dma(sd, dst, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int s = 0; s < nsteps; s += 4) {
+    body(s + 0, 0, frag_stage<1>(), frag_stage<3>());
+    body(s + 1, 1, frag_stage<2>(), frag_stage<0>());
+    body(s + 2, 0, frag_stage<3>(), frag_stage<1>());
+    body(s + 3, 1, frag_stage<0>(), frag_stage<2>());
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  MEDUSA_WAITCNT(0, 0);   // the re-loads past the end land before the block's LDS is handed on
+
+  // epilogue: lane holds D[n + v][m], v < 4, for n = tile + 4*lg, m = tile + lr
+  const bool vec = (N % 4) == 0;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int m = m0 + wm * 128 + g * 16 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int n = n0 + wn * 128 + f * 16 + lg * 4;
+      if (n >= N) continue;
+      const f32x4_t v = acc[f][g];
+      const size_t o = ((size_t)head * M + m) * N + n;
+      if (EPI == kEpiLogits) {
+        if (vec) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t *>(out_f32 + o));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) out_f32[o + e] = v[e];
+        }
+      } else {
+        const u32x2_t hv = *reinterpret_cast<const u32x2_t *>(resid + (size_t)m * H + n);
+        uint16_t hb[4] = {(uint16_t)(hv[0] & 0xffffu), (uint16_t)(hv[0] >> 16), (uint16_t)(hv[1] & 0xffffu),
+                          (uint16_t)(hv[1] >> 16)};
+        uint16_t r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float u = v[e];
+          r[e] = f32_to_bf16_rne(bf16_to_f32(hb[e]) + u / (1.0f + expf(-u)));
+        }
+        const u32x2_t rv = {(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+        *reinterpret_cast<u32x2_t *>(out_bf16 + o) = rv;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+namespace medusa {
+
+size_t packed_rows_bytes(int K, int M, int H) {
+  if (K < 1 || M < 1 || H < 32 || H % 32 != 0) return 0;
+  return (size_t)K * ((M + 15) / 16) * (H / 32) * 1024;
+}
+
+medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int M, int H, uint16_t *Xp) {
+  const size_t lanes = packed_rows_bytes(K, M, H) / 16;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, X, xhs, K, M, H, Xp);
+  return check_launch("pack_rows");
+}
+
+template <int EPI>
+medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
+                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+  if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% 128 != 0 (H=%d)", H);
+  const size_t w_head = (size_t)packed_tiles(N) * (H / 32) * 1024;
+  if (w_head >= (1ull << 32) || packed_rows_bytes(1, M, H) >= (1ull << 32))
+    return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
+  const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
+  if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
+  hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(256), 0, st, Wp, Xp, x_heads, N, H, M, 8,
+                     lgG, resid, ob, of);
+  return check_launch(EPI == kEpiLogits ? "medusa_head_vocab_packed_ws" : "medusa_head_resblock_packed_ws");
+}
+
+template medusa_status head_gemm_fragments<kEpiResblock>(hipStream_t, const uint16_t *, const uint16_t *, int, int,
+                                                         int, int, int, int, const uint16_t *, uint16_t *, float *);
+template medusa_status head_gemm_fragments<kEpiLogits>(hipStream_t, const uint16_t *, const uint16_t *, int, int,
+                                                       int, int, int, int, const uint16_t *, uint16_t *, float *);
+
+}  // namespace medusa
 
 namespace medusa {
 

@@ -151,16 +151,18 @@ class VerifyPass:
         self.r = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")
         self.logits = torch.empty((K, M, V), dtype=torch.float32, device="cuda")
         self.vlogits = torch.empty((1, M, V), dtype=torch.float32, device="cuda")
+        # activations in fragment order for the many-row contractions (shared by the three calls)
+        self.ws = mb.workspace(mb.medusa_head_workspace(K, M, H))
 
     def heads_resblock(self):
-        mb.medusa_head_resblock_packed(self.h, self.step.W1p, self.r)
+        mb.medusa_head_resblock_packed_ws(self.h, self.step.W1p, self.r, self.ws)
 
     def heads_vocab(self):
-        mb.medusa_head_vocab_packed(self.r, self.step.W2p, self.logits)
+        mb.medusa_head_vocab_packed_ws(self.r, self.step.W2p, self.logits, self.ws)
 
     def lm_head(self):
         c = self.step.cfg
-        mb.medusa_head_vocab_packed(self.step.attn.reshape(1, self.M, c.H), self.W_lm, self.vlogits)
+        mb.medusa_head_vocab_packed_ws(self.step.attn.reshape(1, self.M, c.H), self.W_lm, self.vlogits, self.ws)
 
 
 def host_inputs(cfg: configs.Config, T: int, B: int | None = None, L: int | None = None) -> dict:

@@ -111,6 +111,52 @@ def test_packed_equals_row_major_bitwise(group):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("group", [1, 8])
+def test_heads_workspace_calls_equal_packed_bitwise(group):
+    # from 65 rows the workspace calls copy the activations into fragment order
+    # and run the fragment-fed contraction; below that they are the packed calls.
+    # The same products are summed in the same order, so the results are
+    # bit-identical.  Shapes: the row count on either side of the switch, ragged
+    # row and vocabulary tiles (V % 4 != 0: scalar stores), one to five k-loop
+    # trips (H = 128 .. 640), several row and column tiles
+    for K, M, H, V in [(2, 64, 256, 700), (2, 65, 256, 700), (1, 300, 128, 1001), (3, 520, 384, 264),
+                       (2, 257, 640, 2050)]:
+        say("heads workspace", K, M, H, V, "group", group)
+        h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=M + group)
+        W1p, W2p, hd = mb.PackedWeights(dev(W1), group), mb.PackedWeights(dev(W2), group), dev(h)
+        r_a = torch.full((K, M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        r_b = torch.full_like(r_a, float("nan"))
+        lg_a = torch.full((K, M, V), float("nan"), dtype=torch.float32, device="cuda")
+        lg_b = torch.full_like(lg_a, float("nan"))
+        mb.medusa_head_resblock_packed(hd, W1p, r_a)
+        mb.medusa_head_vocab_packed(r_a, W2p, lg_a)
+        ws = mb.workspace(mb.medusa_head_workspace(K, M, H))
+        mb.medusa_head_resblock_packed_ws(hd, W1p, r_b, ws)
+        mb.medusa_head_vocab_packed_ws(r_b, W2p, lg_b, ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(lg_b).any() and not torch.isnan(r_b.float()).any()
+        assert torch.equal(r_a.view(torch.int16), r_b.view(torch.int16))
+        assert torch.equal(lg_a, lg_b)
+
+
+def test_heads_workspace_calls_against_oracle():
+    # the fragment-fed path on its own against the oracle (ragged rows and vocabulary)
+    K, M, H, V = 2, 300, 256, 1001
+    say("heads workspace vs oracle", K, M, H, V)
+    h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=41)
+    r = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")
+    lg = torch.empty((K, M, V), dtype=torch.float32, device="cuda")
+    ws = mb.workspace(mb.medusa_head_workspace(K, M, H))
+    mb.medusa_head_resblock_packed_ws(dev(h), mb.PackedWeights(dev(W1), 8), r, ws)
+    mb.medusa_head_vocab_packed_ws(r, mb.PackedWeights(dev(W2), 8), lg, ws)
+    f = synth.as_f64
+    ref = oracle.medusa_heads(f(h), f(W1), f(W2), round_r_bf16=True)
+    r_ref = oracle.medusa_heads(f(h), f(W1), np.stack([np.eye(H)] * K), round_r_bf16=True)
+    for k in range(K):
+        assert rel_err(host(lg)[k], ref[k]) <= TOL["bf16"], k
+        assert rel_err(host(r)[k], r_ref[k]) <= TOL["bf16"], k
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_pack_layout(group):
     K, N, H = 2, 37, 128

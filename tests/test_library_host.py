@@ -141,6 +141,35 @@ def test_device_calls_validate_before_launch():
     assert mb.lib.medusa_tree_tokens(None, t.handle, 1, 1, 2, fake, fake, fake) == mb.ERR_STATE
 
 
+def test_head_workspace_calls_reject_bad_arguments_before_launch():
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    need = mb.medusa_head_workspace(2, 100, 256)
+    # M >= 65: workspace checks come before anything is enqueued
+    assert mb.lib.medusa_head_vocab_packed_ws(None, 2, 100, 256, 500, 8, fake, fake, fake, fake, need - 1) \
+        == mb.ERR_WORKSPACE
+    assert mb.lib.medusa_head_vocab_packed_ws(None, 2, 100, 256, 500, 8, fake, fake, fake, None, need) == mb.ERR_ARG
+    assert mb.lib.medusa_head_vocab_packed_ws(None, 2, 100, 256, 500, 8, fake, fake, fake, P(0x1008), need) \
+        == mb.ERR_ARG
+    assert b"aligned" in mb.lib.medusa_last_error()
+    assert mb.lib.medusa_head_resblock_packed_ws(None, 2, 100, 256, 3, fake, fake, fake, fake, need) == mb.ERR_ARG
+    assert mb.lib.medusa_head_resblock_packed_ws(None, 2, 100, 256, 8, fake, fake, None, fake, need) == mb.ERR_ARG
+    assert mb.lib.medusa_head_resblock_packed_ws(None, 2, 100, 256, 8, fake, fake, fake, fake, 16) \
+        == mb.ERR_WORKSPACE
+    assert mb.lib.medusa_head_vocab_packed_ws(None, 2, 100, 256, 0, 8, fake, fake, fake, fake, need) == mb.ERR_ARG
+
+
+def test_head_workspace_size():
+    # activations in fragment order: K * ceil(M/16) * (H/32) KiB, from 65 rows on
+    assert mb.medusa_head_workspace(4, 64, 4096) == 0
+    assert mb.medusa_head_workspace(4, 65, 4096) == 4 * 5 * 128 * 1024
+    assert mb.medusa_head_workspace(4, 1024, 4096) == 4 * 64 * 128 * 1024
+    assert mb.medusa_head_workspace(5, 512, 5120) == 5 * 32 * 160 * 1024
+    assert mb.medusa_head_workspace(1, 10912, 4096) == 682 * 128 * 1024
+    assert mb.medusa_head_workspace(2, 100, 100) == 0                  # H % 128 != 0
+    assert mb.medusa_head_workspace(0, 100, 256) == 0
+
+
 def test_workspace_sizes():
     assert mb.medusa_topk_workspace(64, 32000, 10) == 0              # one slice per row
     assert mb.medusa_topk_workspace(4, 70000, 10) == 4 * 3 * 10 * 8   # three sorted lists per row
