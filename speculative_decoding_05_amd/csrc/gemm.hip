@@ -263,28 +263,26 @@ medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X,
 //
 // Block tile 256 (weight rows n) x 256 (activation rows m), one 32-deep
 // reduction step per stage, four stages (4 x 32 KiB of LDS) with the loads for
-// step s+3 issued while step s is computed.  Four waves, one per SIMD, each
-// owning a 128 x 128 sub-tile: 64 v_mfma_f32_16x16x32_bf16 per step from 8 A
-// (weight) and 8 B (activation) fragments, which halves the LDS bytes per
-// matrix-core op against 128 x 64 sub-tiles.  The 256 accumulator registers per
-// lane live in AGPRs; the compiler's own MFMA selection there uses the untied
-// form and permutes all of them every trip, so the MFMA is issued through a
-// tied inline-asm operand ("+a").  The fragments of step s+1 are read into the
-// second register set between the MFMAs of step s (one read per four MFMAs, A
-// fragments first, whose last readers are the first MFMAs of the step before),
-// and the eight loads per wave and step sit between the MFMA groups, so the
-// matrix core starts right after each step's barrier.
+// step s+3 issued while step s is worked on.  Eight waves, two per SIMD, each
+// owning a 128 x 64 sub-tile (32 v_mfma_f32_16x16x32_bf16 per step from 8
+// weight and 4 activation fragments).  Waves 0-3 and 4-7 run half a phase
+// apart ("ping-pong"): while one wave of a SIMD issues its 32 MFMAs at raised
+// priority, the other issues its loads and LDS reads, so the matrix core is
+// fed by one wave while the other fills its registers.  Waves 4-7 take one
+// extra barrier at the start and waves 0-3 one at the end, so every wave
+// passes the same number of barriers.
 //
-// Hazard padding the compiler cannot add around inline asm: s_nop blocks after
-// the accumulators are zeroed and before they are read back.
-//
-// Ordering per step s (vmcnt counts this wave's loads, all into LDS):
-//   wait vmcnt(8)  -> this wave's loads of step s+1 are in LDS (only step s+2's
-//                     eight may be outstanding); lgkmcnt(0) -> step s's fragments
-//                     are in registers
-//   s_barrier      -> every wave's loads of step s+1 are in LDS, and every wave
-//                     has finished reading step s-1's stage, which the loads of
-//                     step s+3 now overwrite ((s+3) % 4 == (s-1) % 4)
+// Ordering, for the wave's memory phase of step s (vmcnt counts this wave's
+// loads, all into LDS):
+//   issue the 4 loads of step s+3 into stage (s+3) % 4 == (s-1) % 4: both wave
+//     groups finished reading step s-1 before the barrier that opened this
+//     phase (each waits lgkmcnt(0) before closing its memory phase)
+//   read step s's 12 fragments; wait vmcnt(8) (this wave's loads of step s+1
+//     are in LDS; only steps s+2, s+3 may be outstanding) and lgkmcnt(0)
+//   barrier; compute phase; barrier
+// A stage is read by waves 0-3 in half-phase 2s and by waves 4-7 in 2s+1;
+// every wave's loads of step s completed in its memory phase of step s-1,
+// which ended by the barrier before half-phase 2s.
 // The stages are four separate __shared__ arrays and the loop is unrolled by
 // four, so the compiler's wait insertion can tell them apart (one shared
 // array would make it wait for every outstanding load before each read).
@@ -308,14 +306,16 @@ __device__ __forceinline__ u32x4_frag_t *frag_stage() {
 #define MEDUSA_WAITCNT(vm, lgkm) \
   __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | ((((vm) >> 4) & 3) << 14) | (7 << 4) | (((lgkm) & 0xF) << 8))
 
-__device__ __forceinline__ void mfma_tied(f32x4_t &c, u32x4_t a, u32x4_t b) {
-  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-}
-
 __device__ __forceinline__ void dma16(const char *g, u32x4_frag_t *l) {
   // address-space casts (C-style: reinterpret_cast cannot change the address space)
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
                                    (void __attribute__((address_space(3))) *)l, 16, 0, 0);
+}
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Activations [K][M][H] (head stride xhs elements) -> fragment order
@@ -340,7 +340,7 @@ __global__ void pack_rows_kernel(const uint16_t *__restrict__ X, long xhs, int K
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void head_gemm_frag(const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp,
+__global__ __launch_bounds__(512, 1) void head_gemm_frag(const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp,
                                                           int x_heads, int N, int H, int M, int GM, int lgG,
                                                           const uint16_t *__restrict__ resid,
                                                           uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
@@ -360,87 +360,76 @@ __global__ __launch_bounds__(256, 1) void head_gemm_frag(const uint16_t *__restr
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS addresses stay scalar
   const int lr = lane & 15, lg = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
+  const int wn = wave & 1, wm = wave >> 1;       // 128 (n) x 64 (m) sub-tile
+  const bool late = wave >= 4;                   // the wave group running half a phase behind
   const int S = H / 32, NT = packed_tiles(N), MT = (M + 15) / 16;
   const char *wbase = reinterpret_cast<const char *>(Wp) + (size_t)head * NT * S * 1024;
   const char *xbase = reinterpret_cast<const char *>(Xp) + (x_heads > 1 ? (size_t)head * MT * S * 1024 : 0);
-  // this wave loads weight fragments (row tiles) 4w..4w+3 and activation fragments 4w..4w+3 of
+  // this wave loads weight fragments (row tiles) 2w, 2w+1 and activation fragments 2w, 2w+1 of
   // the block at every step; tiles past the end re-read the last one (their results are not stored)
-  uint32_t woff[4], xoff[4];
+  uint32_t woff[2], xoff[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = min(n0 / 16 + 4 * wave + j, NT - 1);
+  for (int j = 0; j < 2; ++j) {
+    const int t = min(n0 / 16 + 2 * wave + j, NT - 1);
     woff[j] = (uint32_t)packed_fragment(t, 0, S, lgG) * 1024u + lane * 16u;
-    const int mt = min(m0 / 16 + 4 * wave + j, MT - 1);
+    const int mt = min(m0 / 16 + 2 * wave + j, MT - 1);
     xoff[j] = (uint32_t)mt * S * 1024u + lane * 16u;
   }
   const uint32_t wstep = 1024u << lgG;   // bytes between one row tile's consecutive steps
-  auto dma = [&](int s, u32x4_frag_t *stg, int q) {
-    if (q < 4)
-      dma16(wbase + woff[q] + (uint32_t)s * wstep, stg + (4 * wave + q) * 64);
-    else
-      dma16(xbase + xoff[q - 4] + (uint32_t)s * 1024u, stg + (16 + 4 * wave + q - 4) * 64);
+  auto issue = [&](int s, u32x4_frag_t *stg) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      dma16(wbase + woff[j] + (uint32_t)s * wstep, stg + (2 * wave + j) * 64);
+      dma16(xbase + xoff[j] + (uint32_t)s * 1024u, stg + (16 + 2 * wave + j) * 64);
+    }
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][4];
 #pragma unroll
   for (int f = 0; f < 8; ++f)
 #pragma unroll
-    for (int g = 0; g < 8; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4_t fr[2][16];   // [register set][8 weight fragments, 8 activation fragments]
-  const int aoff = wn * 8 * 64 + lane, boff = (16 + wm * 8) * 64 + lane;
+    for (int g = 0; g < 4; ++g) acc[f][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t a[8], b[4];
+  const int aoff = wn * 8 * 64 + lane, boff = (16 + wm * 4) * 64 + lane;
   const int nsteps = S;   // a multiple of 4 (H % 128 == 0)
 
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dma(0, frag_stage<0>(), q);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dma(min(1, nsteps - 1), frag_stage<1>(), q);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) dma(min(2, nsteps - 1), frag_stage<2>(), q);
-  MEDUSA_WAITCNT(16, 15);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) fr[0][i] = frag_stage<0>()[i < 8 ? aoff + i * 64 : boff + (i - 8) * 64];
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+  issue(0, frag_stage<0>());
+  issue(min(1, nsteps - 1), frag_stage<1>());
+  issue(min(2, nsteps - 1), frag_stage<2>());
+  MEDUSA_WAITCNT(8, 15);   // this wave's loads of step 0 are in LDS
+  block_barrier();         // everyone's are
+  if (late) block_barrier();
 
-  auto body = [&](int s, int set, const u32x4_frag_t *nxt, u32x4_frag_t *dst) {
+  auto body = [&](int s, const u32x4_frag_t *cur, u32x4_frag_t *dst) {
+    issue(min(s + kAhead, nsteps - 1), dst);   // past the end: re-load the last step into a stage never read
+#pragma unroll
+    for (int f = 0; f < 8; ++f) a[f] = cur[aoff + f * 64];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) b[g] = cur[boff + g * 64];
     MEDUSA_WAITCNT(8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    const int sd = min(s + kAhead, nsteps - 1);   // past the end: re-load the last step into a stage never read
+    block_barrier();
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      fr[set ^ 1][i] = nxt[i < 8 ? aoff + i * 64 : boff + (i - 8) * 64];
+    for (int f = 0; f < 8; ++f)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = i * 4 + j, f = q >> 3, g = q & 7;
-        mfma_tied(acc[f][g], fr[set][f], fr[set][8 + g]);
-      }
-      if (i & 1) dma(sd, dst, i >> 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int g = 0; g < 4; ++g) acc[f][g] = mfma(a[f], b[g], acc[f][g]);
+    __builtin_amdgcn_s_setprio(0);
+    block_barrier();
   };
   for (int s = 0; s < nsteps; s += 4) {
-    body(s + 0, 0, frag_stage<1>(), frag_stage<3>());
-    body(s + 1, 1, frag_stage<2>(), frag_stage<0>());
-    body(s + 2, 0, frag_stage<3>(), frag_stage<1>());
-    body(s + 3, 1, frag_stage<0>(), frag_stage<2>());
+    body(s + 0, frag_stage<0>(), frag_stage<3>());
+    body(s + 1, frag_stage<1>(), frag_stage<0>());
+    body(s + 2, frag_stage<2>(), frag_stage<1>());
+    body(s + 3, frag_stage<3>(), frag_stage<2>());
   }
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+  if (!late) block_barrier();
   MEDUSA_WAITCNT(0, 0);   // the re-loads past the end land before the block's LDS is handed on
 
   // epilogue: lane holds D[n + v][m], v < 4, for n = tile + 4*lg, m = tile + lr
   const bool vec = (N % 4) == 0;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int m = m0 + wm * 128 + g * 16 + lr;
+  for (int g = 0; g < 4; ++g) {
+    const int m = m0 + wm * 64 + g * 16 + lr;
     if (m >= M) continue;
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
@@ -497,7 +486,7 @@ medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint
     return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
   const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
   if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
-  hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(256), 0, st, Wp, Xp, x_heads, N, H, M, 8,
+  hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(512), 0, st, Wp, Xp, x_heads, N, H, M, 8,
                      lgG, resid, ob, of);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab_packed_ws" : "medusa_head_resblock_packed_ws");
 }
