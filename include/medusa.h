@@ -153,6 +153,17 @@ medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, int K, int 
 medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                           const void *r, const void *W2p, float *logits, void *ws,
                                           size_t ws_bytes);
+/* Both of the above in one call (as medusa_heads_packed, bit-identical to it):
+ * with M >= 65 the ResBlock also writes r in fragment order into the
+ * workspace, and the vocabulary projection reads it there, so r is not copied
+ * again.  r is still written row-major.
+ *  medusa_heads_workspace(K, M, H): bytes of ws, (K + 1) * ceil(M/16) * (H/32)
+ *                       KiB for M >= 65 and H % 128 == 0, else 0 (then ws may
+ *                       be NULL).  Errors as the calls above. */
+size_t medusa_heads_workspace(int K, int M, int H);
+medusa_status medusa_heads_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group, const void *h,
+                                     const void *W1p, const void *W2p, void *r, float *logits, void *ws,
+                                     size_t ws_bytes);
 
 /* ------------------------------------------------------------------------- */
 /* (2) Top-k of every row.  Tutorial page, sections "候选生成" and "每头 Top-K":

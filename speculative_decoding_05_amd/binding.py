@@ -47,6 +47,8 @@ SIGNATURES = {
     "medusa_head_workspace": (_sz, [_i, _i, _i]),
     "medusa_head_resblock_packed_ws": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_head_vocab_packed_ws": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz]),
+    "medusa_heads_workspace": (_sz, [_i, _i, _i]),
+    "medusa_heads_packed_ws": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _sz]),
     "medusa_topk_workspace": (_sz, [_i, _i, _i]),
     "medusa_topk": (_i, [_p, _i, _i, _i, _p, _p, _p, _p, _sz]),
     "medusa_dense_paths": (_i, [_i, _i, _i, _ip, _ip, ctypes.POINTER(_i)]),
@@ -215,6 +217,23 @@ def medusa_head_vocab_packed_ws(r, W2p, logits, ws=None):
     _dev(ws)
     check(lib.medusa_head_vocab_packed_ws(_stream(), W2p.K, M, W2p.H, W2p.N, W2p.group, _ptr(r), _ptr(W2p.data),
                                           _ptr(logits), _ptr(ws), ws.numel() * ws.element_size()))
+    return logits
+
+
+def medusa_heads_workspace(K, M, H):
+    return lib.medusa_heads_workspace(K, M, H)
+
+
+def medusa_heads_packed_ws(h, W1p, W2p, r, logits, ws=None):
+    _dev(h, r, logits)
+    if W1p.group != W2p.group:
+        raise ValueError("W1p and W2p must share one packing group")
+    M = h.shape[0]
+    if ws is None:
+        ws = workspace(lib.medusa_heads_workspace(W2p.K, M, W2p.H), h.device)
+    _dev(ws)
+    check(lib.medusa_heads_packed_ws(_stream(), W2p.K, M, W2p.H, W2p.N, W2p.group, _ptr(h), _ptr(W1p.data),
+                                     _ptr(W2p.data), _ptr(r), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size()))
     return logits
 
 

@@ -40,10 +40,13 @@ size_t packed_rows_bytes(int K, int M, int H);
 medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int M, int H, uint16_t *Xp);
 // As head_gemm_many_rows with packed weights, the activations given in fragment
 // order: x_heads = 1 shares one packed [M][H] among all heads (the ResBlock's
-// h), x_heads = K gives each head its own.  H % 128 == 0.
+// h), x_heads = K gives each head its own.  H % 128 == 0.  obp (ResBlock only,
+// may be NULL): r written a second time, in fragment order (K heads, as Xp
+// of the vocabulary projection; rows >= M of the last row tile not written).
 template <int EPI>
 medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
-                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of);
+                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of,
+                                  uint16_t *obp);
 // From this many rows the workspace variants of the packed calls run
 // head_gemm_fragments (below it the weight-streaming and 64-row kernels).
 constexpr int kFragmentRows = 65;

@@ -343,7 +343,8 @@ template <int EPI>
 __global__ __launch_bounds__(512, 1) void head_gemm_frag(const uint16_t *__restrict__ Wp, const uint16_t *__restrict__ Xp,
                                                           int x_heads, int N, int H, int M, int GM, int lgG,
                                                           const uint16_t *__restrict__ resid,
-                                                          uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
+                                                          uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32,
+                                                          uint16_t *__restrict__ out_packed) {
   constexpr int BN = 256, BM = 256, kAhead = 3;
   const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
   const int per_head = tiles_n * tiles_m;
@@ -457,6 +458,13 @@ __global__ __launch_bounds__(512, 1) void head_gemm_frag(const uint16_t *__restr
         }
         const u32x2_t rv = {(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
         *reinterpret_cast<u32x2_t *>(out_bf16 + o) = rv;
+        if (out_packed) {
+          // the same four values in fragment order for the next contraction: fragment (row tile
+          // m/16, step n/32) of this head, lane m%16 + 16 * ((n%32)/8), elements n%8 .. +3
+          const size_t fo = (((size_t)head * MT + (m >> 4)) * S + (n >> 5)) * 512 +
+                            (size_t)((m & 15) + 16 * ((n & 31) >> 3)) * 8 + (n & 7);
+          *reinterpret_cast<u32x2_t *>(out_packed + fo) = rv;
+        }
       }
     }
   }
@@ -479,7 +487,7 @@ medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int 
 
 template <int EPI>
 medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
-                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of, uint16_t *obp) {
   if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% 128 != 0 (H=%d)", H);
   const size_t w_head = (size_t)packed_tiles(N) * (H / 32) * 1024;
   if (w_head >= (1ull << 32) || packed_rows_bytes(1, M, H) >= (1ull << 32))
@@ -487,14 +495,16 @@ medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint
   const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
   if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
   hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(512), 0, st, Wp, Xp, x_heads, N, H, M, 8,
-                     lgG, resid, ob, of);
+                     lgG, resid, ob, of, obp);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab_packed_ws" : "medusa_head_resblock_packed_ws");
 }
 
 template medusa_status head_gemm_fragments<kEpiResblock>(hipStream_t, const uint16_t *, const uint16_t *, int, int,
-                                                         int, int, int, int, const uint16_t *, uint16_t *, float *);
+                                                         int, int, int, int, const uint16_t *, uint16_t *, float *,
+                                                         uint16_t *);
 template medusa_status head_gemm_fragments<kEpiLogits>(hipStream_t, const uint16_t *, const uint16_t *, int, int,
-                                                       int, int, int, int, const uint16_t *, uint16_t *, float *);
+                                                       int, int, int, int, const uint16_t *, uint16_t *, float *,
+                                                       uint16_t *);
 
 }  // namespace medusa
 

@@ -442,7 +442,7 @@ extern "C" medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, 
   uint16_t *hp = static_cast<uint16_t *>(ws);
   if ((s = pack_rows(st, hb, 0, 1, M, H, hp)) != MEDUSA_OK) return s;   // one h shared by every head
   return head_gemm_fragments<kEpiResblock>(st, static_cast<const uint16_t *>(W1p), hp, 1, K, H, H, M, lgG, hb,
-                                           static_cast<uint16_t *>(r), nullptr);
+                                           static_cast<uint16_t *>(r), nullptr, nullptr);
 }
 
 extern "C" medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
@@ -463,7 +463,45 @@ extern "C" medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int
   uint16_t *rp = static_cast<uint16_t *>(ws);
   if ((s = pack_rows(st, static_cast<const uint16_t *>(r), (long)M * H, K, M, H, rp)) != MEDUSA_OK) return s;
   return head_gemm_fragments<kEpiLogits>(st, static_cast<const uint16_t *>(W2p), rp, K, K, V, H, M, lgG, nullptr,
-                                         nullptr, logits);
+                                         nullptr, logits, nullptr);
+}
+
+// Both projections in one call: the ResBlock's epilogue writes r row-major
+// (the output) and again in fragment order into the workspace, where the
+// vocabulary projection reads it, so r is not copied a second time.
+extern "C" size_t medusa_heads_workspace(int K, int M, int H) {
+  if (K < 1 || M < kFragmentRows || H < 128 || H % 128 != 0) return 0;
+  return packed_rows_bytes(K + 1, M, H);   // packed h, then packed r of the K heads
+}
+
+extern "C" medusa_status medusa_heads_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
+                                                const void *h, const void *W1p, const void *W2p, void *r,
+                                                float *logits, void *ws, size_t ws_bytes) {
+  if (M < kFragmentRows || H % 128 != 0)
+    return medusa_heads_packed(stream, K, M, H, V, group, h, W1p, W2p, r, logits);
+  const char *who = "medusa_heads_packed_ws";
+  medusa_status s = check_common(who, MEDUSA_BF16, K, M, H);
+  if (s != MEDUSA_OK) return s;
+  const int lgG = group_log2(group);
+  if (lgG < 0) return fail(MEDUSA_ERR_ARG, "%s: group=%d not in {1, 2, 4, 8}", who, group);
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "%s: V=%d", who, V);
+  if (!h || !W1p || !W2p || !r || !logits) return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
+  if (!aligned16(h) || !aligned16(W1p) || !aligned16(W2p) || !aligned16(r) || !aligned16(logits))
+    return fail(MEDUSA_ERR_ARG, "%s: pointers must be 16-byte aligned", who);
+  const size_t need = medusa_heads_workspace(K, M, H);
+  if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  if (!ws) return fail(MEDUSA_ERR_ARG, "%s: NULL workspace", who);
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+  hipStream_t st = as_stream(stream);
+  const uint16_t *hb = static_cast<const uint16_t *>(h);
+  uint16_t *hp = static_cast<uint16_t *>(ws);
+  uint16_t *rp = hp + packed_rows_bytes(1, M, H) / sizeof(uint16_t);
+  if ((s = pack_rows(st, hb, 0, 1, M, H, hp)) != MEDUSA_OK) return s;
+  if ((s = head_gemm_fragments<kEpiResblock>(st, static_cast<const uint16_t *>(W1p), hp, 1, K, H, H, M, lgG, hb,
+                                             static_cast<uint16_t *>(r), nullptr, rp)) != MEDUSA_OK)
+    return s;
+  return head_gemm_fragments<kEpiLogits>(st, static_cast<const uint16_t *>(W2p), rp, K, K, V, H, M, lgG, nullptr,
+                                         nullptr, logits, nullptr);
 }
 
 extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,

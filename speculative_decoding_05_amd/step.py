@@ -151,14 +151,18 @@ class VerifyPass:
         self.r = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")
         self.logits = torch.empty((K, M, V), dtype=torch.float32, device="cuda")
         self.vlogits = torch.empty((1, M, V), dtype=torch.float32, device="cuda")
-        # activations in fragment order for the many-row contractions (shared by the three calls)
-        self.ws = mb.workspace(mb.medusa_head_workspace(K, M, H))
+        # activations in fragment order for the many-row contractions (shared by the calls)
+        self.ws = mb.workspace(max(mb.medusa_head_workspace(K, M, H), mb.medusa_heads_workspace(K, M, H)))
 
     def heads_resblock(self):
         mb.medusa_head_resblock_packed_ws(self.h, self.step.W1p, self.r, self.ws)
 
     def heads_vocab(self):
         mb.medusa_head_vocab_packed_ws(self.r, self.step.W2p, self.logits, self.ws)
+
+    def heads(self):
+        """ResBlock and vocabulary projection in one call (r not copied twice)."""
+        mb.medusa_heads_packed_ws(self.h, self.step.W1p, self.step.W2p, self.r, self.logits, self.ws)
 
     def lm_head(self):
         c = self.step.cfg

@@ -135,11 +135,20 @@ def test_verify_pass_full_size(name):
     h_nodes, W_lm = synth.node_hidden(cfg, M), synth.lm_head_weights(cfg)
     s = st.Step(cfg, tree, hostin)
     vp = st.VerifyPass(s, h_nodes=h_nodes, W_lm=W_lm)
+    # the separate calls, then the combined one (which the bench's verify pass runs):
+    # bit-identical at full size, and the combined one's outputs go to the oracle
     vp.heads_resblock()
     vp.heads_vocab()
+    r_sep, lg_sep = vp.r.clone(), vp.logits.clone()
+    vp.r.fill_(float("nan"))
+    vp.logits.fill_(float("nan"))
+    vp.heads()
     s.attention()
     vp.lm_head()
     torch.cuda.synchronize()
+    assert torch.equal(vp.r.view(torch.int16), r_sep.view(torch.int16))
+    assert torch.equal(vp.logits, lg_sep)
+    del r_sep, lg_sep
     H, V, K = cfg.H, cfg.V, cfg.K
     g = np.random.default_rng(cfg.cfg_id + 5)
     rows = np.sort(g.choice(M, 4, replace=False))

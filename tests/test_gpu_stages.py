@@ -139,6 +139,30 @@ def test_heads_workspace_calls_equal_packed_bitwise(group):
         assert torch.equal(lg_a, lg_b)
 
 
+@pytest.mark.parametrize("group", [1, 8])
+def test_heads_combined_workspace_call_equals_packed_bitwise(group):
+    # one call for both projections: the ResBlock also writes r in fragment
+    # order into the workspace and the vocabulary projection reads it there
+    for K, M, H, V in [(2, 64, 256, 700), (2, 65, 256, 700), (1, 300, 128, 1001), (3, 520, 384, 264),
+                       (2, 257, 640, 2050)]:
+        say("heads combined workspace", K, M, H, V, "group", group)
+        h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=3 * M + group)
+        W1p, W2p, hd = mb.PackedWeights(dev(W1), group), mb.PackedWeights(dev(W2), group), dev(h)
+        r_a = torch.full((K, M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        r_b = torch.full_like(r_a, float("nan"))
+        lg_a = torch.full((K, M, V), float("nan"), dtype=torch.float32, device="cuda")
+        lg_b = torch.full_like(lg_a, float("nan"))
+        mb.medusa_heads_packed(hd, W1p, W2p, r_a, lg_a)
+        # the workspace starts as garbage (NaN bits): nothing may depend on what it held
+        ws = mb.workspace(mb.medusa_heads_workspace(K, M, H))
+        ws.fill_(0xFF)
+        mb.medusa_heads_packed_ws(hd, W1p, W2p, r_b, lg_b, ws)
+        torch.cuda.synchronize()
+        assert not torch.isnan(lg_b).any()
+        assert torch.equal(r_a.view(torch.int16), r_b.view(torch.int16))
+        assert torch.equal(lg_a, lg_b)
+
+
 def test_heads_workspace_calls_against_oracle():
     # the fragment-fed path on its own against the oracle (ragged rows and vocabulary)
     K, M, H, V = 2, 300, 256, 1001

@@ -159,6 +159,23 @@ def test_head_workspace_calls_reject_bad_arguments_before_launch():
     assert mb.lib.medusa_head_vocab_packed_ws(None, 2, 100, 256, 0, 8, fake, fake, fake, fake, need) == mb.ERR_ARG
 
 
+def test_heads_combined_workspace_call_rejects_bad_arguments_before_launch():
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    need = mb.medusa_heads_workspace(2, 100, 256)
+    assert need == mb.medusa_head_workspace(3, 100, 256)          # packed h + packed r of 2 heads
+    args = [None, 2, 100, 256, 500, 8, fake, fake, fake, fake, fake]
+    assert mb.lib.medusa_heads_packed_ws(*args, fake, need - 16) == mb.ERR_WORKSPACE
+    assert mb.lib.medusa_heads_packed_ws(*args, None, need) == mb.ERR_ARG
+    assert mb.lib.medusa_heads_packed_ws(*args, P(0x1008), need) == mb.ERR_ARG
+    assert mb.lib.medusa_heads_packed_ws(None, 2, 100, 256, 500, 5, fake, fake, fake, fake, fake, fake, need) \
+        == mb.ERR_ARG
+    assert mb.lib.medusa_heads_packed_ws(None, 2, 100, 256, 500, 8, fake, fake, None, fake, fake, fake, need) \
+        == mb.ERR_ARG
+    assert mb.medusa_heads_workspace(4, 64, 4096) == 0
+    assert mb.medusa_heads_workspace(4, 1024, 4096) == 5 * 64 * 128 * 1024
+
+
 def test_head_workspace_size():
     # activations in fragment order: K * ceil(M/16) * (H/32) KiB, from 65 rows on
     assert mb.medusa_head_workspace(4, 64, 4096) == 0
