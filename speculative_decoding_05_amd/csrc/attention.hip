@@ -65,6 +65,7 @@ __device__ __forceinline__ uint2 read_tr(const uint16_t *p) {
 
 struct Split {
   int nsplit, per_split;  // keys of the prefix per slice (multiple of kKT)
+  bool three_per_cu;      // the 168-register build that runs three blocks per CU
 };
 
 // Prefix slices per (b, head): measured on MI355X, split partials plus the
@@ -80,19 +81,30 @@ inline Split split_into(int L, int ns) {
   per = (per + kKT - 1) / kKT * kKT;
   if (per == 0) per = kKT;
   ns = L > 0 ? (L + per - 1) / per : 1;
-  return {ns, per};
+  return {ns, per, false};
 }
 
 inline Split choose_split(int B, int nh, int T, int L) {
   const int qb = kQB * qtiles_for(T);
   const long pairs = (long)B * nh * ((T + qb - 1) / qb);
   int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
-  // between one and two blocks per CU, the CUs that get two set the time;
-  // three slices even the load out (measured: 13B shape, 320 pairs, 4096 keys)
-  if (pairs > kCUs && pairs < 2 * kCUs) ns = 3;
+  // Between one and two (b, head) pairs per CU the CUs that get two set the
+  // time.  With one query tile per wave the kernel also builds in 168
+  // registers, which runs three blocks per CU: two slices then fill
+  // 2 * pairs <= 768 block slots in one round, with half again the loads in
+  // flight per CU (measured, 13B shape, 320 pairs, 4096 keys: 128.6 -> 119.3 us
+  // with the merge; three slices at two blocks per CU before).  Elsewhere the
+  // 168-register build is slower (batch 1: 16.2 -> 17.5 us).
+  bool three = false;
+  if (pairs > kCUs && pairs < 2 * kCUs) {
+    three = qtiles_for(T) == 1;
+    ns = three ? 2 : 3;
+  }
   const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
   if (ns > max_ns) ns = max_ns;
-  return split_into(L, ns);
+  Split sp = split_into(L, ns);
+  sp.three_per_cu = three;
+  return sp;
 }
 
 template <int DH>
@@ -141,8 +153,8 @@ __device__ __forceinline__ void store_tile(const TileRegs<DH> &t, uint16_t (*ks)
 // one prefix slice.  With QT = 2 every K/V fragment read from LDS feeds two
 // MFMAs and the two tiles' softmax and MFMA streams interleave.
 // STAGES tiles are prefetched into registers ahead of the one being consumed.
-template <int DH, int QT, int STAGES>
-__global__ __launch_bounds__(kThreads, 2) void tree_attn_bf16(
+template <int DH, int QT, int STAGES, int MINB>
+__global__ __launch_bounds__(kThreads, MINB) void tree_attn_bf16(
     int B, int nh, int T, int W, int L, int Lstride, const int32_t *__restrict__ seq_len, float scale_log2,
     int qgroups, int nsplit, int per_split, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt, const uint16_t *__restrict__ vt,
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const uint64_t *__restrict__ mask,
@@ -560,7 +572,12 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
     ws_o = static_cast<float *>(ws);
     ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
   }
-  hipLaunchKernelGGL((tree_attn_bf16<DH, QT, STAGES>), dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
+  // blocks per CU the build is made for: three only for one query tile per wave
+  auto kern = tree_attn_bf16<DH, QT, STAGES, 2>;
+  if constexpr (QT == 1) {
+    if (sp.three_per_cu) kern = tree_attn_bf16<DH, QT, STAGES, 3>;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
                      t->W, L, pf.Lstride, pf.seq_len, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),

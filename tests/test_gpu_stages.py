@@ -322,6 +322,10 @@ CHAIN5 = [[0] * d for d in range(1, 6)]
     ("bf16", "dense32", 2, 2, 128, 0),         # empty prefix
     ("bf16", "dense32", 1, 1, 128, 1),
     ("bf16", "greedy64", 2, 4, 128, 256),
+    # 300 (b, head) pairs, between one and two per CU: the three-blocks-per-CU build
+    # with two prefix slices (the second ragged: 280 keys)
+    ("bf16", "greedy64", 2, 150, 128, 600),
+    ("bf16", "dense32", 3, 100, 64, 600),
     ("f32", "dense22", 1, 4, 64, 128),         # the tiny fp32 configuration
     ("f32", "dense32", 2, 2, 128, 77),
 ])
