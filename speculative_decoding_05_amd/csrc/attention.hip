@@ -394,8 +394,12 @@ __global__ __launch_bounds__(kThreads, MINB) void tree_attn_bf16(
   }
 }
 
-// Merge the slices of one (b, h, node) row: weights 2^(m_s - M).
-template <int DH>
+// Merge the slices of one (b, h, node) row: weights 2^(m_s - M).  NS > 0:
+// every slice's (m, l) and partial O are loaded in one round, NS loads each
+// (slices past nsplit re-load the last one and are not summed); NS = 0: a loop
+// over the slices.  The launcher passes NS = nsplit for 2-4 slices, so no load
+// is wasted there, and 8 for 5-8.
+template <int DH, int NS>
 __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T, int nsplit,
                                                             const float *__restrict__ ws_o,
                                                             const float2 *__restrict__ ws_ml,
@@ -408,23 +412,22 @@ __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T
   const size_t stride = (size_t)nrows;
   float l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (nsplit <= kMergeUnroll) {
-    // every slice's (m, l) and partial O are loaded in one round
-    float2 ml[kMergeUnroll];
-    float4 po[kMergeUnroll];
+  if (NS > 0) {
+    float2 ml[NS > 0 ? NS : 1];
+    float4 po[NS > 0 ? NS : 1];
     float M = -INFINITY;
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s) {
+    for (int s = 0; s < NS; ++s) {
       const int sl = s < nsplit ? s : nsplit - 1;
       ml[s] = ws_ml[sl * stride + row];
       po[s] = *reinterpret_cast<const float4 *>(ws_o + (sl * stride + row) * DH + c);
     }
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s)
+    for (int s = 0; s < NS; ++s)
       if (s < nsplit) M = fmaxf(M, ml[s].x);
     const float Mu = M == -INFINITY ? 0.f : M;
 #pragma unroll
-    for (int s = 0; s < kMergeUnroll; ++s)
+    for (int s = 0; s < NS; ++s)
       if (s < nsplit) {
         const float w = exp2f(ml[s].x - Mu);
         l += w * ml[s].y;
@@ -587,7 +590,12 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
   if (s != MEDUSA_OK || sp.nsplit == 1) return s;
   const long rows = (long)B * nh * t->T;
   const int rpb = 256 / (DH / 4);
-  hipLaunchKernelGGL((tree_attn_merge_bf16<DH>), dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+  auto merge = sp.nsplit == 2 ? tree_attn_merge_bf16<DH, 2>
+             : sp.nsplit == 3 ? tree_attn_merge_bf16<DH, 3>
+             : sp.nsplit == 4 ? tree_attn_merge_bf16<DH, 4>
+             : sp.nsplit <= kMergeUnroll ? tree_attn_merge_bf16<DH, kMergeUnroll>
+                                         : tree_attn_merge_bf16<DH, 0>;
+  hipLaunchKernelGGL(merge, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
                      B, nh, t->T, sp.nsplit, ws_o, ws_ml, static_cast<uint16_t *>(out));
   return check_launch("tree_attention merge");
 }
