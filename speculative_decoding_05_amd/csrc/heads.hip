@@ -246,8 +246,9 @@ void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, 
 // stream, that limit these), with two waves splitting the reduction.
 // ResBlock (N = H, few tiles): more waves per block split the reduction so
 // enough loads are in flight (16 waves x 4 k-steps for up to 4 rows, 8 waves
-// up to 16 rows, and for 17-32 rows 8 waves of four row tiles sharing each
-// activation fragment).
+// up to 8 rows, and for 9-32 rows 8 waves of four row tiles sharing each
+// activation fragment; at 16 rows that took the 7B ResBlock from 26.4 to
+// 22.3 us, at 5 rows it would be slower).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
                           int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
@@ -255,8 +256,10 @@ medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, 
   const int m0 = 0, Mg = M;   // one group: the weights are streamed once
   if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
     launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
-  else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
+  else if (EPI == EPI_RESBLOCK && Mg <= 8 && H % (32 * 8) == 0)
     launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+  else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
+    launch_one<4, 1, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
     launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4)
