@@ -111,7 +111,7 @@ def test_packed_equals_row_major_bitwise(group):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("group", [1, 8])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_heads_workspace_calls_equal_packed_bitwise(group):
     # from 65 rows the workspace calls copy the activations into fragment order
     # and run the fragment-fed contraction; below that they are the packed calls.
@@ -139,7 +139,7 @@ def test_heads_workspace_calls_equal_packed_bitwise(group):
         assert torch.equal(lg_a, lg_b)
 
 
-@pytest.mark.parametrize("group", [1, 8])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_heads_combined_workspace_call_equals_packed_bitwise(group):
     # one call for both projections: the ResBlock also writes r in fragment
     # order into the workspace and the vocabulary projection reads it there
@@ -161,6 +161,32 @@ def test_heads_combined_workspace_call_equals_packed_bitwise(group):
         assert not torch.isnan(lg_b).any()
         assert torch.equal(r_a.view(torch.int16), r_b.view(torch.int16))
         assert torch.equal(lg_a, lg_b)
+
+
+def test_heads_workspace_calls_take_no_workspace_below_65_rows():
+    # below 65 rows the workspace calls are the packed calls: a NULL workspace of
+    # zero bytes is accepted, and the results are the packed calls' bit for bit
+    K, H, V = 2, 256, 700
+    for M in (1, 16, 64):
+        assert mb.medusa_head_workspace(K, M, H) == 0 and mb.medusa_heads_workspace(K, M, H) == 0
+        h, W1, W2 = head_inputs("bf16", K, M, H, V, seed=500 + M)
+        g = mb.medusa_pack_group_for_rows(M)
+        W1p, W2p, hd = mb.PackedWeights(dev(W1), g), mb.PackedWeights(dev(W2), g), dev(h)
+        r_a = torch.empty((K, M, H), dtype=torch.bfloat16, device="cuda")
+        lg_a = torch.empty((K, M, V), dtype=torch.float32, device="cuda")
+        mb.medusa_heads_packed(hd, W1p, W2p, r_a, lg_a)
+        r_b, r_c = torch.empty_like(r_a), torch.empty_like(r_a)
+        lg_b, lg_c = torch.empty_like(lg_a), torch.empty_like(lg_a)
+        mb.check(mb.lib.medusa_heads_packed_ws(mb._stream(), K, M, H, V, g, mb._ptr(hd), mb._ptr(W1p.data),
+                                               mb._ptr(W2p.data), mb._ptr(r_b), mb._ptr(lg_b), None, 0))
+        mb.check(mb.lib.medusa_head_resblock_packed_ws(mb._stream(), K, M, H, g, mb._ptr(hd), mb._ptr(W1p.data),
+                                                       mb._ptr(r_c), None, 0))
+        mb.check(mb.lib.medusa_head_vocab_packed_ws(mb._stream(), K, M, H, V, g, mb._ptr(r_c), mb._ptr(W2p.data),
+                                                    mb._ptr(lg_c), None, 0))
+        torch.cuda.synchronize()
+        for r in (r_b, r_c):
+            assert torch.equal(r_a.view(torch.int16), r.view(torch.int16)), M
+        assert torch.equal(lg_a, lg_b) and torch.equal(lg_a, lg_c), M
 
 
 def test_heads_workspace_calls_against_oracle():
