@@ -27,6 +27,30 @@ def oracle_ragged_attention(q, kt, vt, kc, vc, lens, tree):
     return np.stack(out)
 
 
+def test_ragged_attention_three_blocks_per_cu():
+    # 300 (b, head) pairs of a tree of at most 64 tokens: the three-blocks-per-CU
+    # build with two prefix slices, over ragged lengths (an empty prefix, a
+    # slice boundary inside a tile, a full second slice)
+    p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10
+    ot = oracle.build_tree(p, K, k)
+    t = mb.Tree(p, K, k).upload()
+    lens, nh, dh, L_cap = [0, 333, 600], 100, 128, 640
+    B, T = len(lens), ot["T"]
+    say("ragged attention, three blocks per CU", B, nh, dh, L_cap, lens)
+    g = rng(4242)
+    mk = lambda shape: store(g.standard_normal(shape).astype(np.float32), "bf16")
+    q, kt, vt = mk((B, T, nh, dh)), mk((B, T, nh, dh)), mk((B, T, nh, dh))
+    kc, vc = mk((B, nh, L_cap, dh)), mk((B, nh, L_cap, dh))
+    out = torch.full((B, T, nh, dh), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mb.tree_attention_ragged(t, dev(q), dev(kt), dev(vt), dev(kc), dev(vc), dev(np.array(lens, np.int32)),
+                             max(lens), out)
+    ref = oracle_ragged_attention(q, kt, vt, kc, vc, lens, ot)
+    got = host(out)
+    for b in range(B):
+        for h in range(nh):
+            assert rel_err(got[b, :, h], ref[b, :, h]) <= TOL["bf16"], (b, h)
+
+
 @pytest.mark.parametrize("dtype,paths,dh,L_cap,lens", [
     ("bf16", "greedy64", 128, 700, [0, 64, 300, 651, 700]),   # several prefix slices
     ("bf16", "dense22", 64, 90, [5, 0, 90]),
