@@ -47,6 +47,10 @@ template <int EPI>
 medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
                                   int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of,
                                   uint16_t *obp);
+// The shape limits of head_gemm_fragments (H % 128 == 0, each head's packed
+// operands under 4 GiB, the grid under 2^31 blocks), checked before anything
+// is enqueued: MEDUSA_OK or the error (message set).
+medusa_status fragments_supported(int K, int N, int H, int M);
 // From this many rows the workspace variants of the packed calls run
 // head_gemm_fragments (below it the weight-streaming and 64-row kernels).
 constexpr int kFragmentRows = 65;

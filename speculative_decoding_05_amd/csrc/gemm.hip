@@ -485,15 +485,22 @@ medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int 
   return check_launch("pack_rows");
 }
 
-template <int EPI>
-medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
-                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of, uint16_t *obp) {
+medusa_status fragments_supported(int K, int N, int H, int M) {
   if (H % 128 != 0) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: H %% 128 != 0 (H=%d)", H);
   const size_t w_head = (size_t)packed_tiles(N) * (H / 32) * 1024;
   if (w_head >= (1ull << 32) || packed_rows_bytes(1, M, H) >= (1ull << 32))
     return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: one head's operands exceed 4 GiB (N=%d M=%d H=%d)", N, M, H);
   const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
   if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
+  return MEDUSA_OK;
+}
+
+template <int EPI>
+medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint16_t *Xp, int x_heads, int K, int N,
+                                  int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of, uint16_t *obp) {
+  medusa_status s = fragments_supported(K, N, H, M);
+  if (s != MEDUSA_OK) return s;
+  const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
   hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(512), 0, st, Wp, Xp, x_heads, N, H, M, 8,
                      lgG, resid, ob, of, obp);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab_packed_ws" : "medusa_head_resblock_packed_ws");

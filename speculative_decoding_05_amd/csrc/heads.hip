@@ -440,6 +440,7 @@ extern "C" medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, 
   if (!aligned16(h) || !aligned16(W1p) || !aligned16(r))
     return fail(MEDUSA_ERR_ARG, "%s: pointers must be 16-byte aligned", who);
   if ((s = check_ws(who, K, M, H, ws, ws_bytes)) != MEDUSA_OK) return s;
+  if ((s = fragments_supported(K, H, H, M)) != MEDUSA_OK) return s;      // before anything is enqueued
   hipStream_t st = as_stream(stream);
   const uint16_t *hb = static_cast<const uint16_t *>(h);
   uint16_t *hp = static_cast<uint16_t *>(ws);
@@ -462,6 +463,7 @@ extern "C" medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int
   if (!aligned16(r) || !aligned16(W2p) || !aligned16(logits))
     return fail(MEDUSA_ERR_ARG, "%s: pointers must be 16-byte aligned", who);
   if ((s = check_ws(who, K, M, H, ws, ws_bytes)) != MEDUSA_OK) return s;
+  if ((s = fragments_supported(K, V, H, M)) != MEDUSA_OK) return s;      // before anything is enqueued
   hipStream_t st = as_stream(stream);
   uint16_t *rp = static_cast<uint16_t *>(ws);
   if ((s = pack_rows(st, static_cast<const uint16_t *>(r), (long)M * H, K, M, H, rp)) != MEDUSA_OK) return s;
@@ -495,6 +497,9 @@ extern "C" medusa_status medusa_heads_packed_ws(medusa_stream_t stream, int K, i
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
   if (!ws) return fail(MEDUSA_ERR_ARG, "%s: NULL workspace", who);
   if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
+  // both contractions' limits before anything is enqueued
+  if ((s = fragments_supported(K, H, H, M)) != MEDUSA_OK || (s = fragments_supported(K, V, H, M)) != MEDUSA_OK)
+    return s;
   hipStream_t st = as_stream(stream);
   const uint16_t *hb = static_cast<const uint16_t *>(h);
   uint16_t *hp = static_cast<uint16_t *>(ws);

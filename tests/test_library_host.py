@@ -176,6 +176,22 @@ def test_heads_combined_workspace_call_rejects_bad_arguments_before_launch():
     assert mb.medusa_heads_workspace(4, 1024, 4096) == 5 * 64 * 128 * 1024
 
 
+def test_head_workspace_calls_check_shape_limits_before_launch():
+    # one head's packed activations over 4 GiB: refused as unsupported before any
+    # launch (on this host a launch would fail with ERR_HIP instead)
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    M, H = 600000, 4096                      # 37500 row tiles x 128 KiB = 4.6 GiB per head
+    huge = 1 << 40
+    assert mb.lib.medusa_head_vocab_packed_ws(None, 1, M, H, 1000, 8, fake, fake, fake, fake, huge) \
+        == mb.ERR_UNSUPPORTED
+    assert b"4 GiB" in mb.lib.medusa_last_error()
+    assert mb.lib.medusa_head_resblock_packed_ws(None, 1, M, H, 8, fake, fake, fake, fake, huge) \
+        == mb.ERR_UNSUPPORTED
+    assert mb.lib.medusa_heads_packed_ws(None, 1, M, H, 1000, 8, fake, fake, fake, fake, fake, fake, huge) \
+        == mb.ERR_UNSUPPORTED
+
+
 def test_head_workspace_size():
     # activations in fragment order: K * ceil(M/16) * (H/32) KiB, from 65 rows on
     assert mb.medusa_head_workspace(4, 64, 4096) == 0
