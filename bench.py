@@ -116,7 +116,14 @@ def verify_pass(s, reps):
     # one call (the verify pass runs that one, then the LM head)
     fns = {"heads_resblock": vp.heads_resblock, "heads_vocab": vp.heads_vocab, "heads": vp.heads,
            "lm_head": vp.lm_head}
-    out = {"rows": M, "us": {}, "tflops": {}, "mfma_frac": {}}
+    # algorithmic HBM bytes (weights, activations and outputs once each): at few
+    # rows the contractions stream weights, and this rate is the one that binds
+    e = 2  # bf16
+    hbm = {"heads_resblock": K * H * H * e + M * H * e * 2 + K * M * H * e,
+           "heads_vocab": K * V * H * e + K * M * H * e + K * M * V * 4,
+           "heads": K * (H + V) * H * e + M * H * e * 2 + K * M * H * e + K * M * V * 4,
+           "lm_head": V * H * e + M * H * e + M * V * 4}
+    out = {"rows": M, "us": {}, "tflops": {}, "mfma_frac": {}, "hbm_gbps": {}}
     for name, fn in fns.items():
         fn()
         torch.cuda.synchronize()
@@ -135,6 +142,7 @@ def verify_pass(s, reps):
         out["us"][name] = us
         out["tflops"][name] = flops[name] / (us * 1e-6) / 1e12
         out["mfma_frac"][name] = flops[name] / (us * 1e-6) / BF16_PEAK
+        out["hbm_gbps"][name] = hbm[name] / (us * 1e-6) / 1e9
     tot_f = flops["heads"] + flops["lm_head"]
     tot_us = out["us"]["heads"] + out["us"]["lm_head"]
     out["total"] = {"us": tot_us, "tflops": tot_f / (tot_us * 1e-6) / 1e12,
