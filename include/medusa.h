@@ -32,6 +32,23 @@
  *    medusa_last_error() returns a thread-local description.  A failed launch
  *    returns MEDUSA_ERR_HIP.  Faults inside kernels surface at the caller's
  *    next synchronisation.  No C++ exception crosses this interface.
+ *
+ * Debug environment variables (read by the device calls; off by default):
+ *  - MEDUSA_VALIDATE=1: before their kernels, medusa_topk and
+ *    medusa_topk_tree_tokens check the logits for NaN and the root tokens
+ *    for ids outside [0, V); typical_accept and rejection_accept check their
+ *    logits for NaN and +inf and the tree tokens for ids outside [0, V).  A
+ *    finding returns MEDUSA_ERR_NONFINITE (logits) or MEDUSA_ERR_ARG (ids)
+ *    and enqueues nothing else, so the outputs are untouched.  The check is
+ *    one extra kernel plus a synchronisation of `stream`, so it is refused
+ *    (MEDUSA_ERR_STATE) while the stream is being captured into a graph.
+ *    Without it, NaN logits give unspecified results, an out-of-range
+ *    candidate token is never accepted, and an out-of-range root token is
+ *    copied as it is.
+ *  - MEDUSA_FAULT=launch: every kernel launch fails before it is enqueued;
+ *    the call returns MEDUSA_ERR_HIP with nothing enqueued (error-path tests).
+ *  - MEDUSA_TRACE=1: each device call is wrapped in a roctx range of its
+ *    name (rocprofv3 --marker-trace); roctx is opened at run time.
  */
 #ifndef MEDUSA_H
 #define MEDUSA_H
@@ -53,7 +70,10 @@ typedef enum {
   MEDUSA_ERR_UNSUPPORTED = 4,  /* valid request outside the supported limits        */
   MEDUSA_ERR_WORKSPACE = 5,    /* workspace smaller than the *_workspace size       */
   MEDUSA_ERR_HIP = 6,          /* a HIP runtime call or kernel launch failed        */
-  MEDUSA_ERR_STATE = 7         /* tree not uploaded to the device                   */
+  MEDUSA_ERR_STATE = 7,        /* tree not uploaded to the device; validate mode    */
+                               /* asked for under graph capture                     */
+  MEDUSA_ERR_NONFINITE = 8     /* NaN (or, for acceptance, +inf) logits; reported   */
+                               /* only with MEDUSA_VALIDATE=1                       */
 } medusa_status;
 
 typedef enum { MEDUSA_F32 = 0, MEDUSA_BF16 = 1 } medusa_dtype;

@@ -19,8 +19,9 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m speculative_decoding_05_amd.build`")
 lib = ctypes.CDLL(LIB_PATH)
 
-OK, ERR_ARG, ERR_SHAPE, ERR_TREE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_STATE = range(8)
-STATUS_NAMES = ["OK", "ERR_ARG", "ERR_SHAPE", "ERR_TREE", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_HIP", "ERR_STATE"]
+OK, ERR_ARG, ERR_SHAPE, ERR_TREE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_STATE, ERR_NONFINITE = range(9)
+STATUS_NAMES = ["OK", "ERR_ARG", "ERR_SHAPE", "ERR_TREE", "ERR_UNSUPPORTED", "ERR_WORKSPACE", "ERR_HIP", "ERR_STATE",
+                "ERR_NONFINITE"]
 F32, BF16 = 0, 1
 MAX_TOPK, MAX_TREE = 64, 1024
 

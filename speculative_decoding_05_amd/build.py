@@ -3,7 +3,8 @@
     python -m speculative_decoding_05_amd.build        (or __graft_entry__.build())
 
 Every .hip source under csrc/ is compiled to an object under _build/ at the
-repository root (in parallel), then linked into one shared library next to
+repository root (in parallel), the host-only tree code (tree.cpp) with the
+system C++ compiler, then all are linked into one shared library next to
 this file.  Packed-fp32 instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -20,7 +21,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmedusa_hip.so")
-SOURCES = ["host.hip", "heads.hip", "gemm.hip", "topk.hip", "attention.hip", "accept.hip", "rejection.hip", "commit.hip"]
+SOURCES = ["host.hip", "heads.hip", "gemm.hip", "topk.hip", "attention.hip", "accept.hip", "rejection.hip", "commit.hip",
+           "debug.hip"]
+# host-only C++ (no HIP headers): built with the system C++ compiler
+CXX_SOURCES = ["tree.cpp"]
 ARCH = "gfx950"
 
 
@@ -37,9 +41,20 @@ def flags():
             "-I", INCLUDE, "-I", CSRC]
 
 
+def cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("no C++ compiler found")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if src in CXX_SOURCES:
+        cmd = [cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC,
+               "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -48,11 +63,12 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    srcs = SOURCES + CXX_SOURCES
+    jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-ldl"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

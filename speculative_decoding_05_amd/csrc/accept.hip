@@ -270,8 +270,10 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
     float p;
     bool dec;
     if (greedy) {
-      dec = tok == s_amax[sl];
-      p = dec ? 1.f : 0.f;
+      // one-hot p at the argmax: H = 0, so the threshold is min(eps, delta)
+      // and the argmax token is kept iff 1 > that threshold
+      p = tok == s_amax[sl] ? 1.f : 0.f;
+      dec = p > s_thr[sl];
     } else if (tok < 0 || tok >= V) {  // out-of-range id: never accepted
       p = 0.f;
       dec = false;
@@ -363,6 +365,7 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
                                         float delta, float temperature, int32_t *accept_len,
                                         int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
                                         float *cand_p, float *row_thr, void *ws, size_t ws_bytes) {
+  TraceRange tr("typical_accept");
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (B < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "typical_accept: B=%d V=%d", B, V);
@@ -375,17 +378,28 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
   const size_t need = typical_accept_workspace(t, B, V);
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = as_stream(stream);
+  if (validate_enabled()) {  // NaN / +inf logits; tree tokens outside [0, V)
+    ValidateSpec v;
+    v.a = logits;
+    v.na = (size_t)B * t->T * V;
+    v.posinf_bad = true;
+    v.tok = tree_tok;
+    v.nt = (size_t)B * t->T;
+    v.V = V;
+    s = validate_inputs(st, "typical_accept", v);
+    if (s != MEDUSA_OK) return s;
+  }
   const int nchunks = chunks_for(V);
   const int greedy = temperature == 0.f;
   const float inv_tau = greedy ? 1.f : 1.f / temperature;
   Part *part = static_cast<Part *>(ws);
   if (t->n_internal > 0) {
-    hipLaunchKernelGGL((accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
+    MEDUSA_LAUNCH("typical_accept", (accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
                        logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
     s = check_launch("typical_accept row pass");
     if (s != MEDUSA_OK) return s;
   }
-  hipLaunchKernelGGL(accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
+  MEDUSA_LAUNCH("typical_accept", accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
                      t->depth_max, t->n_internal, nchunks, t->d_slot, t->d_parent, t->d_depth, t->d_mask,
                      eps, delta, inv_tau, greedy, part, accept_len, best_node, next_tok, accepted_tok,
                      cand_p, row_thr);

@@ -44,7 +44,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMinKeysPerSplit = 256;
 constexpr int kSplitTargetBlocks = 128;
 constexpr int kMergeUnroll = 8;       // slices the merge loads in one round
-constexpr long kCUs = 256;     // compute units of the device
 
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -96,7 +95,8 @@ inline Split choose_split(int B, int nh, int T, int L) {
   // with the merge; three slices at two blocks per CU before).  Elsewhere the
   // 168-register build is slower (batch 1: 16.2 -> 17.5 us).
   bool three = false;
-  if (pairs > kCUs && pairs < 2 * kCUs) {
+  const long cus = device_compute_units();
+  if (pairs > cus && pairs < 2 * cus) {
     three = qtiles_for(T) == 1;
     ns = three ? 2 : 3;
   }
@@ -580,7 +580,7 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
   if constexpr (QT == 1) {
     if (sp.three_per_cu) kern = tree_attn_bf16<DH, QT, STAGES, 3>;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
+  MEDUSA_LAUNCH("tree_attention", kern, dim3((unsigned)nblocks), dim3(kThreads), 0, st, B, nh, t->T,
                      t->W, L, pf.Lstride, pf.seq_len, scale * kLog2e, qgroups, sp.nsplit, sp.per_split,
                      static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
                      static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
@@ -595,7 +595,7 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
              : sp.nsplit == 4 ? tree_attn_merge_bf16<DH, 4>
              : sp.nsplit <= kMergeUnroll ? tree_attn_merge_bf16<DH, kMergeUnroll>
                                          : tree_attn_merge_bf16<DH, 0>;
-  hipLaunchKernelGGL(merge, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+  MEDUSA_LAUNCH("tree_attention", merge, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
                      B, nh, t->T, sp.nsplit, ws_o, ws_ml, static_cast<uint16_t *>(out));
   return check_launch("tree_attention merge");
 }
@@ -605,7 +605,7 @@ medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, Pr
                          const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
                          const void *v_cache, void *out) {
   const int qgroups = (t->T + kF32Q - 1) / kF32Q;
-  hipLaunchKernelGGL((tree_attn_f32<DH>), dim3(B * nh * qgroups), dim3(256), 0, st, B, nh, t->T, t->W, pf.L,
+  MEDUSA_LAUNCH("tree_attention", (tree_attn_f32<DH>), dim3(B * nh * qgroups), dim3(256), 0, st, B, nh, t->T, t->W, pf.L,
                      pf.Lstride, pf.seq_len, scale, qgroups, static_cast<const float *>(q), static_cast<const float *>(k_tree),
                      static_cast<const float *>(v_tree), static_cast<const float *>(k_cache),
                      static_cast<const float *>(v_cache), t->d_mask, static_cast<float *>(out));
@@ -666,6 +666,7 @@ extern "C" medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt,
                                         int B, int nh, int dh, int L, float scale, const void *q,
                                         const void *k_tree, const void *v_tree, const void *k_cache,
                                         const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+  TraceRange tr("tree_attention");
   return attention_entry("tree_attention", stream, dt, t, B, nh, dh, Prefix{L, L, nullptr}, scale, q, k_tree,
                          v_tree, k_cache, v_cache, out, ws, ws_bytes);
 }
@@ -675,6 +676,7 @@ extern "C" medusa_status tree_attention_ragged(medusa_stream_t stream, medusa_dt
                                                const int32_t *seq_len, float scale, const void *q,
                                                const void *k_tree, const void *v_tree, const void *k_cache,
                                                const void *v_cache, void *out, void *ws, size_t ws_bytes) {
+  TraceRange tr("tree_attention_ragged");
   if (!seq_len) return fail(MEDUSA_ERR_ARG, "tree_attention_ragged: NULL seq_len");
   if (L_max > L_cap) return fail(MEDUSA_ERR_ARG, "tree_attention_ragged: L_max=%d > L_cap=%d", L_max, L_cap);
   return attention_entry("tree_attention_ragged", stream, dt, t, B, nh, dh, Prefix{L_max, L_cap, seq_len}, scale,

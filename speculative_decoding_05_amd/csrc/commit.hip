@@ -63,6 +63,7 @@ extern "C" medusa_status medusa_kv_commit(medusa_stream_t stream, medusa_dtype d
                                           int nh, int dh, int L_cap, const void *k_tree, const void *v_tree,
                                           const int32_t *best_node, int32_t *seq_len, void *k_cache,
                                           void *v_cache, const int32_t *next_tok, int32_t *root_tok) {
+  TraceRange tr("medusa_kv_commit");
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (dt != MEDUSA_F32 && dt != MEDUSA_BF16) return fail(MEDUSA_ERR_ARG, "medusa_kv_commit: unknown dtype");
@@ -76,7 +77,7 @@ extern "C" medusa_status medusa_kv_commit(medusa_stream_t stream, medusa_dtype d
     return fail(MEDUSA_ERR_ARG, "medusa_kv_commit: next_tok and root_tok go together");
   if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(MEDUSA_ERR_ARG, "medusa_kv_commit: K/V pointers must be 16-byte aligned");
-  hipLaunchKernelGGL(kv_commit_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, nh, dh * esize / 16,
+  MEDUSA_LAUNCH("medusa_kv_commit", kv_commit_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, nh, dh * esize / 16,
                      L_cap, t->d_parent, t->d_depth, static_cast<const u32x4_t *>(k_tree),
                      static_cast<const u32x4_t *>(v_tree), best_node, seq_len, static_cast<u32x4_t *>(k_cache),
                      static_cast<u32x4_t *>(v_cache), next_tok, root_tok);

@@ -7,36 +7,47 @@
 #include <vector>
 
 #include "medusa.h"
-
-// Candidate tree: host arrays plus one device copy (see medusa_tree_upload).
-struct medusa_tree {
-  int K = 0, k = 0, T = 0, W = 0, depth_max = 0, n_leaves = 0, n_internal = 0;
-  std::vector<int32_t> parent, depth, rank, retrieve;
-  std::vector<int32_t> internal;  // nodes with children, ascending
-  std::vector<int32_t> slot;      // node -> index in `internal`, -1 for leaves
-  std::vector<int32_t> dstart;    // [depth_max + 2]: nodes of depth d are dstart[d] .. dstart[d+1]-1
-  std::vector<uint64_t> mask;     // [T][W]
-  // per group of 16 consecutive nodes: bit w set iff some node of the group
-  // has an ancestor (or is itself) among nodes 64w .. 64w+63
-  std::vector<uint32_t> tile_need;  // [ceil(T/16)]
-  // device copy (valid after upload)
-  void *d_base = nullptr;
-  int device = -1;
-  const uint64_t *d_mask = nullptr;
-  const int32_t *d_parent = nullptr, *d_depth = nullptr, *d_rank = nullptr;
-  const int32_t *d_internal = nullptr, *d_slot = nullptr, *d_dstart = nullptr;
-  const uint32_t *d_tile_need = nullptr;
-};
+#include "tree.h"
 
 namespace medusa {
 
-medusa_status fail(medusa_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-void clear_error();
 medusa_status check_launch(const char *what);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline hipStream_t as_stream(medusa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 medusa_status check_tree_on_device(const medusa_tree *t);
+// Debug facilities (environment variables, see debug.hip).
+bool fault_injected();    // MEDUSA_FAULT=launch: every launch fails before it is enqueued
+bool validate_enabled();  // MEDUSA_VALIDATE=1: device checks of the inputs before the kernels
+class TraceRange {        // MEDUSA_TRACE=1: roctx range for the lifetime of the object
+ public:
+  explicit TraceRange(const char *name);
+  ~TraceRange();
+  TraceRange(const TraceRange &) = delete;
+  TraceRange &operator=(const TraceRange &) = delete;
+
+ private:
+  bool on_ = false;
+};
+// What validate mode checks: up to two float arrays (NaN, and +inf where
+// posinf_bad, is an error) and one int32 token array (ids outside [0, V)).
+struct ValidateSpec {
+  const float *a = nullptr;
+  size_t na = 0;
+  const float *b = nullptr;
+  size_t nb = 0;
+  bool posinf_bad = false;
+  const int32_t *tok = nullptr;
+  size_t nt = 0;
+  int V = 0;
+};
+// Runs the checks on `st` and waits for them; ERR_NONFINITE / ERR_ARG on a
+// finding, ERR_STATE under graph capture.
+medusa_status validate_inputs(hipStream_t st, const char *who, const ValidateSpec &v);
+
+// compute units of the current device (queried once per device; 256 if the
+// query fails)
+int device_compute_units();
 
 // bf16 helpers (bit patterns held in uint16)
 __host__ __device__ inline float bf16_to_f32(uint16_t b) {
@@ -108,3 +119,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 }  // namespace medusa
+
+// Launch through the fault gate: with MEDUSA_FAULT=launch the enclosing call
+// returns MEDUSA_ERR_HIP before anything is enqueued.
+#define MEDUSA_LAUNCH(who, ...)                                                                   \
+  do {                                                                                            \
+    if (medusa::fault_injected())                                                                 \
+      return medusa::fail(MEDUSA_ERR_HIP, "%s: injected launch failure (MEDUSA_FAULT=launch)", who); \
+    hipLaunchKernelGGL(__VA_ARGS__);                                                              \
+  } while (0)

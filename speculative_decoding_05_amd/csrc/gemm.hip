@@ -242,7 +242,7 @@ medusa_status launch_tiled(hipStream_t st, const uint16_t *W, const uint16_t *X,
   }
   const long blocks = (long)K * ((N + BN - 1) / BN) * ((M + BM - 1) / BM);
   if (blocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "head projection: %ld tiles", blocks);
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(S::kThreads), S::kLdsBytes, st, W, X, xhs, N, H, M,
+  MEDUSA_LAUNCH("medusa heads (many rows)", kern, dim3((unsigned)blocks), dim3(S::kThreads), S::kLdsBytes, st, W, X, xhs, N, H, M,
                      GM, lgG, resid, ob, of);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab (tiled)" : "medusa_head_resblock (tiled)");
 }
@@ -481,7 +481,7 @@ size_t packed_rows_bytes(int K, int M, int H) {
 
 medusa_status pack_rows(hipStream_t st, const uint16_t *X, long xhs, int K, int M, int H, uint16_t *Xp) {
   const size_t lanes = packed_rows_bytes(K, M, H) / 16;
-  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, X, xhs, K, M, H, Xp);
+  MEDUSA_LAUNCH("medusa heads (many rows)", pack_rows_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st, X, xhs, K, M, H, Xp);
   return check_launch("pack_rows");
 }
 
@@ -501,7 +501,7 @@ medusa_status head_gemm_fragments(hipStream_t st, const uint16_t *Wp, const uint
   medusa_status s = fragments_supported(K, N, H, M);
   if (s != MEDUSA_OK) return s;
   const long blocks = (long)K * ((N + 255) / 256) * ((M + 255) / 256);
-  hipLaunchKernelGGL(head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(512), 0, st, Wp, Xp, x_heads, N, H, M, 8,
+  MEDUSA_LAUNCH("medusa heads (many rows)", head_gemm_frag<EPI>, dim3((unsigned)blocks), dim3(512), 0, st, Wp, Xp, x_heads, N, H, M, 8,
                      lgG, resid, ob, of, obp);
   return check_launch(EPI == kEpiLogits ? "medusa_head_vocab_packed_ws" : "medusa_head_resblock_packed_ws");
 }

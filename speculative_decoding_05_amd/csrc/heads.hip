@@ -232,11 +232,12 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__res
 }
 
 template <int R, int C, int EPI, bool PACKED, int U, int NW>
-void launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
+medusa_status launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
                 int m0, int Mg, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
   const int tiles = (N + 16 * R - 1) / (16 * R);
-  hipLaunchKernelGGL((head_gemm_bf16<R, C, EPI, PACKED, U, NW>), dim3(tiles * K), dim3(64 * NW), 0, st, W, X, xhs,
+  MEDUSA_LAUNCH("medusa heads", (head_gemm_bf16<R, C, EPI, PACKED, U, NW>), dim3(tiles * K), dim3(64 * NW), 0, st, W, X, xhs,
                      N, H, M, m0, Mg, tiles, lgG, resid, ob, of);
+  return MEDUSA_OK;
 }
 
 // Tiling by shape (measured on MI355X).  Vocabulary projection (N = V, many
@@ -254,26 +255,28 @@ medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, 
                           int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
   if (M >= kManyRows) return head_gemm_many_rows<EPI, PACKED>(st, W, X, xhs, K, N, H, M, lgG, resid, ob, of);
   const int m0 = 0, Mg = M;   // one group: the weights are streamed once
+  medusa_status s;
   if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
-    launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_RESBLOCK && Mg <= 8 && H % (32 * 8) == 0)
-    launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
-    launch_one<4, 1, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<4, 1, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
-    launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 4)
-    launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_LOGITS && Mg > 8 && Mg <= 16)
-    launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (EPI == EPI_LOGITS && Mg > 16)
-    launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (Mg <= 16)
-    launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else if (H % (32 * 8) == 0)
-    launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
   else
-    launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+  if (s != MEDUSA_OK) return s;
   return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
 }
 
@@ -282,7 +285,7 @@ medusa_status launch_f32(hipStream_t st, const float *W, const float *X, long xh
                          int H, int M, const float *resid, float *out) {
   const long waves = (long)K * N * ((M + 7) / 8);
   const dim3 grid((unsigned)((waves + 3) / 4));
-  hipLaunchKernelGGL((head_gemm_f32<EPI>), grid, dim3(256), 0, st, W, X, xhs, K, N, H, M, resid, out);
+  MEDUSA_LAUNCH("medusa heads", (head_gemm_f32<EPI>), grid, dim3(256), 0, st, W, X, xhs, K, N, H, M, resid, out);
   return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
 }
 
@@ -300,6 +303,7 @@ medusa_status check_common(const char *who, medusa_dtype dt, int K, int M, int H
 
 extern "C" medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dtype dt, int K, int M,
                                               int H, const void *h, const void *W1, void *r) {
+  TraceRange tr("medusa_head_resblock");
   medusa_status s = check_common("medusa_head_resblock", dt, K, M, H);
   if (s != MEDUSA_OK) return s;
   if (!h || !W1 || !r) return fail(MEDUSA_ERR_ARG, "medusa_head_resblock: NULL pointer");
@@ -317,6 +321,7 @@ extern "C" medusa_status medusa_head_resblock(medusa_stream_t stream, medusa_dty
 extern "C" medusa_status medusa_head_vocab(medusa_stream_t stream, medusa_dtype dt, int K, int M,
                                            int H, int V, const void *r, const void *W2,
                                            float *logits) {
+  TraceRange tr("medusa_head_vocab");
   medusa_status s = check_common("medusa_head_vocab", dt, K, M, H);
   if (s != MEDUSA_OK) return s;
   if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab: V=%d", V);
@@ -335,6 +340,7 @@ extern "C" medusa_status medusa_head_vocab(medusa_stream_t stream, medusa_dtype 
 extern "C" medusa_status medusa_heads(medusa_stream_t stream, medusa_dtype dt, int K, int M, int H,
                                       int V, const void *h, const void *W1, const void *W2, void *r,
                                       float *logits) {
+  TraceRange tr("medusa_heads");
   medusa_status s = check_common("medusa_heads", dt, K, M, H);
   if (s != MEDUSA_OK) return s;
   if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_heads: V=%d", V);
@@ -368,6 +374,7 @@ extern "C" int medusa_pack_group_for_rows(int M) { return M <= 8 ? 1 : kPackGrou
 
 extern "C" medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int N, int H, int group,
                                              const void *W, void *Wp) {
+  TraceRange tr("medusa_pack_weights");
   if (K < 1 || N < 1 || H < 1) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: K=%d N=%d H=%d", K, N, H);
   const int lgG = group_log2(group);
   if (lgG < 0) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: group=%d not in {1, 2, 4, 8}", group);
@@ -375,13 +382,14 @@ extern "C" medusa_status medusa_pack_weights(medusa_stream_t stream, int K, int 
   if (!W || !Wp) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: NULL pointer");
   if (!aligned16(W) || !aligned16(Wp)) return fail(MEDUSA_ERR_ARG, "medusa_pack_weights: pointers must be 16-byte aligned");
   const size_t lanes = medusa_packed_weight_bytes(K, N, H) / 16;
-  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, as_stream(stream),
+  MEDUSA_LAUNCH("medusa heads", pack_weights_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, as_stream(stream),
                      static_cast<const uint16_t *>(W), static_cast<uint16_t *>(Wp), K, N, H, lgG);
   return check_launch("medusa_pack_weights");
 }
 
 extern "C" medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int K, int M, int H, int group,
                                                      const void *h, const void *W1p, void *r) {
+  TraceRange tr("medusa_head_resblock_packed");
   medusa_status s = check_common("medusa_head_resblock_packed", MEDUSA_BF16, K, M, H);
   if (s != MEDUSA_OK) return s;
   const int lgG = group_log2(group);
@@ -396,6 +404,7 @@ extern "C" medusa_status medusa_head_resblock_packed(medusa_stream_t stream, int
 
 extern "C" medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                                   const void *r, const void *W2p, float *logits) {
+  TraceRange tr("medusa_head_vocab_packed");
   medusa_status s = check_common("medusa_head_vocab_packed", MEDUSA_BF16, K, M, H);
   if (s != MEDUSA_OK) return s;
   const int lgG = group_log2(group);
@@ -430,6 +439,7 @@ static medusa_status check_ws(const char *who, int K, int M, int H, const void *
 extern "C" medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, int K, int M, int H, int group,
                                                         const void *h, const void *W1p, void *r, void *ws,
                                                         size_t ws_bytes) {
+  TraceRange tr("medusa_head_resblock_packed_ws");
   if (M < kFragmentRows || H % 128 != 0) return medusa_head_resblock_packed(stream, K, M, H, group, h, W1p, r);
   const char *who = "medusa_head_resblock_packed_ws";
   medusa_status s = check_common(who, MEDUSA_BF16, K, M, H);
@@ -452,6 +462,7 @@ extern "C" medusa_status medusa_head_resblock_packed_ws(medusa_stream_t stream, 
 extern "C" medusa_status medusa_head_vocab_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                                      const void *r, const void *W2p, float *logits, void *ws,
                                                      size_t ws_bytes) {
+  TraceRange tr("medusa_head_vocab_packed_ws");
   if (M < kFragmentRows || H % 128 != 0) return medusa_head_vocab_packed(stream, K, M, H, V, group, r, W2p, logits);
   const char *who = "medusa_head_vocab_packed_ws";
   medusa_status s = check_common(who, MEDUSA_BF16, K, M, H);
@@ -482,6 +493,7 @@ extern "C" size_t medusa_heads_workspace(int K, int M, int H) {
 extern "C" medusa_status medusa_heads_packed_ws(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                                 const void *h, const void *W1p, const void *W2p, void *r,
                                                 float *logits, void *ws, size_t ws_bytes) {
+  TraceRange tr("medusa_heads_packed_ws");
   if (M < kFragmentRows || H % 128 != 0)
     return medusa_heads_packed(stream, K, M, H, V, group, h, W1p, W2p, r, logits);
   const char *who = "medusa_heads_packed_ws";
@@ -515,6 +527,7 @@ extern "C" medusa_status medusa_heads_packed_ws(medusa_stream_t stream, int K, i
 extern "C" medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                              const void *h, const void *W1p, const void *W2p, void *r,
                                              float *logits) {
+  TraceRange tr("medusa_heads_packed");
   medusa_status s = check_common("medusa_heads_packed", MEDUSA_BF16, K, M, H);
   if (s != MEDUSA_OK) return s;
   if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_heads_packed: V=%d", V);

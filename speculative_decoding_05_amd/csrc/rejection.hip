@@ -285,6 +285,7 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
                                           float temperature, const float *u_node, const float *u_bonus,
                                           int32_t *accept_len, int32_t *best_node, int32_t *next_tok,
                                           int32_t *accepted_tok, float *keep_prob) {
+  TraceRange tr("rejection_accept");
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (B < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "rejection_accept: B=%d V=%d", B, V);
@@ -295,7 +296,20 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
   if (!logits || !head_logits || !tree_tok || !u_node || !u_bonus || !accept_len || !best_node || !next_tok ||
       !accepted_tok)
     return fail(MEDUSA_ERR_ARG, "rejection_accept: NULL pointer");
-  hipLaunchKernelGGL(rejection_accept_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V,
+  if (validate_enabled()) {  // NaN / +inf logits of either distribution; tree tokens outside [0, V)
+    ValidateSpec v;
+    v.a = logits;
+    v.na = (size_t)B * t->T * V;
+    v.b = head_logits;
+    v.nb = (size_t)K * B * V;
+    v.posinf_bad = true;
+    v.tok = tree_tok;
+    v.nt = (size_t)B * t->T;
+    v.V = V;
+    s = validate_inputs(as_stream(stream), "rejection_accept", v);
+    if (s != MEDUSA_OK) return s;
+  }
+  MEDUSA_LAUNCH("rejection_accept", rejection_accept_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V,
                      t->depth_max, t->d_parent, t->d_depth, t->d_dstart, logits, head_logits, B, tree_tok,
                      temperature, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
   return check_launch("rejection_accept");

@@ -73,11 +73,12 @@ struct TokenScatter {
 __device__ __forceinline__ void scatter_tokens(const TokenScatter &ts, int row, const uint64_t *s_out) {
   if (!ts.tree_tok) return;
   const int head = row / ts.B, b = row % ts.B;
+  // the root first: a root-only tree (depth_max = 0) has no node to scatter
+  if (head == 0 && threadIdx.x == 0) ts.tree_tok[(size_t)b * ts.T] = ts.root[b];
   if (head + 1 > ts.depth_max) return;
   const int j0 = ts.dstart[head + 1], j1 = ts.dstart[head + 2];
   for (int j = j0 + (int)threadIdx.x; j < j1; j += blockDim.x)
     ts.tree_tok[(size_t)b * ts.T + j] = static_cast<int32_t>(key_index(s_out[ts.rank[j]]));
-  if (head == 0 && threadIdx.x == 0) ts.tree_tok[(size_t)b * ts.T] = ts.root[b];
 }
 
 // idx/val/scatter of a finished row from its sorted keys
@@ -263,7 +264,8 @@ extern "C" size_t medusa_topk_workspace(int R, int V, int k) {
 }
 
 static medusa_status topk_launch(const char *who, hipStream_t st, int R, int V, int k, const float *logits,
-                                 int32_t *idx, float *val, void *ws, size_t ws_bytes, const TokenScatter &ts) {
+                                 int32_t *idx, float *val, void *ws, size_t ws_bytes, const TokenScatter &ts,
+                                 int n_root = 0) {
   if (R < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "%s: R=%d V=%d", who, R, V);
   if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "%s: k=%d outside [1, V=%d]", who, k, V);
   if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: k=%d > %d", who, k, MEDUSA_MAX_TOPK);
@@ -277,16 +279,27 @@ static medusa_status topk_launch(const char *who, hipStream_t st, int R, int V, 
   if (need > 0 && (reinterpret_cast<uintptr_t>(ws) & 7u))
     return fail(MEDUSA_ERR_ARG, "%s: workspace must be 8-byte aligned", who);
   if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: R=%d > 65535", who, R);
+  if (validate_enabled()) {  // NaN logits; root tokens outside [0, V)
+    ValidateSpec v;
+    v.a = logits;
+    v.na = (size_t)R * V;
+    v.tok = ts.root;
+    v.nt = ts.root ? (size_t)n_root : 0;
+    v.V = V;
+    medusa_status vs = validate_inputs(st, who, v);
+    if (vs != MEDUSA_OK) return vs;
+  }
   uint64_t *part = static_cast<uint64_t *>(ws);
-  hipLaunchKernelGGL((topk_slices<kNT, kPT>), dim3(ns, R), dim3(kNT), 0, st, logits, V, k, ns, idx, val, part, ts);
+  MEDUSA_LAUNCH("medusa_topk", (topk_slices<kNT, kPT>), dim3(ns, R), dim3(kNT), 0, st, logits, V, k, ns, idx, val, part, ts);
   medusa_status s = check_launch(who);
   if (s != MEDUSA_OK || ns == 1) return s;
-  hipLaunchKernelGGL(topk_merge, dim3(R), dim3(kMergeThreads), 0, st, logits, V, k, ns, part, idx, val, ts);
+  MEDUSA_LAUNCH("medusa_topk", topk_merge, dim3(R), dim3(kMergeThreads), 0, st, logits, V, k, ns, part, idx, val, ts);
   return check_launch(who);
 }
 
 extern "C" medusa_status medusa_topk(medusa_stream_t stream, int R, int V, int k, const float *logits,
                                      int32_t *idx, float *val, void *ws, size_t ws_bytes) {
+  TraceRange tr("medusa_topk");
   const TokenScatter none = {nullptr, nullptr, nullptr, nullptr, 1, 1, 0};
   return topk_launch("medusa_topk", as_stream(stream), R, V, k, logits, idx, val, ws, ws_bytes, none);
 }
@@ -295,6 +308,7 @@ extern "C" medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const m
                                                  int V, int k, const float *logits, const int32_t *root_tok,
                                                  int32_t *topk_idx, int32_t *tree_tok, void *ws,
                                                  size_t ws_bytes) {
+  TraceRange tr("medusa_topk_tree_tokens");
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (B < 1 || K < 1) return fail(MEDUSA_ERR_ARG, "medusa_topk_tree_tokens: B=%d K=%d", B, K);
@@ -304,12 +318,13 @@ extern "C" medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const m
                 K, k, t->depth_max, t->k);
   const TokenScatter ts = {tree_tok, t->d_rank, t->d_dstart, root_tok, B, t->T, t->depth_max};
   return topk_launch("medusa_topk_tree_tokens", as_stream(stream), K * B, V, k, logits, topk_idx, nullptr, ws,
-                     ws_bytes, ts);
+                     ws_bytes, ts, B);
 }
 
 extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B,
                                             int K, int k, const int32_t *root_tok,
                                             const int32_t *topk_idx, int32_t *tree_tok) {
+  TraceRange tr("medusa_tree_tokens");
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (B < 1) return fail(MEDUSA_ERR_ARG, "medusa_tree_tokens: B=%d", B);
@@ -318,7 +333,7 @@ extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa
     return fail(MEDUSA_ERR_SHAPE, "medusa_tree_tokens: top-k block [K=%d][k=%d] smaller than the tree's [%d][%d]",
                 K, k, t->depth_max, t->k);
   const int n = B * t->T;
-  hipLaunchKernelGGL(tree_tokens_kernel, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), B,
+  MEDUSA_LAUNCH("medusa_topk", tree_tokens_kernel, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream), B,
                      t->T, k, t->d_depth, t->d_rank, root_tok, topk_idx, tree_tok);
   return check_launch("medusa_tree_tokens");
 }

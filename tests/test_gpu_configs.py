@@ -3,15 +3,21 @@ times (packed head weights, the library's split choice).
 
 The GPU runs the chained step; the oracle runs its own chain on the same
 seeded inputs (never on GPU outputs):
-  heads     full GPU logits vs oracle logits on sampled vocabulary rows;
+  heads     every logit of every head and row against the oracle's logits,
+            and the ResBlock output r;
   top-k     GPU indices vs the oracle's (from its float64 logits), bit-exact on
             every row whose sorted top-(k+1) values are separated by >= 1e-3
             (closer rows are flagged: fp32 vs fp64 logits may order them
             differently), plus an exact check on synthetic logits fed to both;
   tokens    bit-exact on unflagged sequences;
-  attention sampled (b, head) slices;
+  attention every (b, head) slice up to 512 slices (tiny, 7B batch 1, 7B batch
+            16), else 24 slices that include the first and the last;
   accept    verification logits planted at the oracle's candidates, fed to
             both; flag rule of typical_accept parity.
+Further acceptance cases at the full shapes, on logits fed to both sides:
+moderate-entropy rows (geometric profile over a random top list, tokens at
+their parent's ranks) and rows whose candidates sit right at the threshold
+(many flagged decisions).
 """
 import numpy as np
 import pytest
@@ -33,6 +39,21 @@ def oracle_tree(cfg):
     paths = (oracle.dense_paths(cfg.K, spec.k) if spec.kind == "dense"
              else oracle.greedy_paths(configs.acc_exact, cfg.K, spec.n_paths, spec.rank_cap))
     return oracle.build_tree(paths, cfg.K, spec.k)
+
+
+def attention_slices(cfg, n_sampled=24, full_up_to=512):
+    """All (b, head) pairs when there are at most full_up_to of them; else
+    n_sampled distinct pairs including (0, 0) and (B-1, nh-1).  Every pair
+    covers all of its prefix slices and query groups (all T queries are
+    compared)."""
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.nh)]
+    if len(pairs) <= full_up_to:
+        return pairs
+    g = np.random.default_rng(cfg.cfg_id + 2)
+    pick = {0, len(pairs) - 1}
+    while len(pick) < n_sampled:
+        pick.add(int(g.integers(len(pairs))))
+    return [pairs[i] for i in sorted(pick)]
 
 
 def topk_flagged(vals_sorted, k):
@@ -62,18 +83,16 @@ def test_config_chain(name):
     h64, W1 = f(hostin["h"]), f(hostin["W1"])
     eye_r = oracle.medusa_heads(h64, W1, np.stack([np.eye(cfg.H)] * K), round_r_bf16=rnd)
     assert rel_err(r_g, eye_r) <= TOL[cfg.dtype]
-    rows = np.random.default_rng(cfg.cfg_id).choice(V, 384, replace=False)
-    ref_rows = oracle.medusa_heads(h64, W1, f(hostin["W2"][:, rows]), round_r_bf16=rnd)
-    for kk in range(K):
-        assert rel_err(lg_g[kk][:, rows], ref_rows[kk]) <= TOL[cfg.dtype], kk
+    W2_64 = f(hostin["W2"])
+    lo = oracle.medusa_heads(h64, W1, W2_64, round_r_bf16=rnd)
+    del W2_64
+    for kk in range(K):                      # every logit of head kk, all rows
+        assert rel_err(lg_g[kk], lo[kk]) <= TOL[cfg.dtype], kk
 
     # ---- top-k and tree tokens: the oracle's own chain
     s.topk_and_tokens()
     idx_g = host(s.topk_idx).astype(np.int64)
     tok_g = host(s.tree_tok).astype(np.int64)
-    W2_64 = f(hostin["W2"])
-    lo = oracle.medusa_heads(h64, W1, W2_64, round_r_bf16=rnd)
-    del W2_64
     idx_o, val_o = oracle.topk_per_head(lo, k)
     full_o = -np.sort(-lo.reshape(K * B, V), axis=1)[:, :k + 1]
     flag = topk_flagged(full_o, k).reshape(K, B)
@@ -93,11 +112,11 @@ def test_config_chain(name):
     mb.medusa_topk(dev(zl), k, zi, None, s.ws_topk)
     assert np.array_equal(host(zi), oracle.medusa_topk(zl.astype(np.float64), k)[0])
 
-    # ---- tree attention, sampled (b, head) slices
+    # ---- tree attention: every (b, head) slice, or 24 of them at the two largest shapes
     s.attention()
     att = host(s.attn)
-    g = np.random.default_rng(cfg.cfg_id + 2)
-    sel = sorted({(int(g.integers(B)), int(g.integers(cfg.nh))) for _ in range(3)} | {(B - 1, cfg.nh - 1)})
+    sel = attention_slices(cfg)
+    say("  attention slices checked:", len(sel), "of", B * cfg.nh)
     ref = oracle.tree_attention(f(hostin["q"]), f(hostin["kt"]), f(hostin["vt"]), f(hostin["kc"]),
                                 f(hostin["vc"]), ot, None, sel)
     for b, hh in sel:
@@ -166,3 +185,80 @@ def test_verify_pass_full_size(name):
                                       f(hostin["kc"][sl]), f(hostin["vc"][sl]), ot)
         z_ref = oracle.verification_logits(o_ref.reshape(1, tree.T, H), f(W_lm[cols]))[0]
         assert rel_err(z[b][:, cols], z_ref) <= TOL["bf16"], b
+
+
+def moderate_entropy_rows(g, T, V, top=60):
+    """Rows of one sequence: a geometric profile z = -lam * r (lam ~ U(0.4, 1.2)
+    per row, plus N(0, 0.3^2) noise) over `top` random tokens in rank order r,
+    the other tokens far below (-40).  Entropy of 1-2 nats, thresholds
+    0.05-0.09.  Returns the rows and each row's ranked token list."""
+    z = (-40.0 + 0.3 * g.standard_normal((T, V))).astype(np.float32)
+    order = np.empty((T, top), np.int64)
+    for n in range(T):
+        order[n] = g.choice(V, top, replace=False)
+        lam = g.uniform(0.4, 1.2)
+        z[n, order[n]] = (-lam * np.arange(top) + 0.3 * g.standard_normal(top)).astype(np.float32)
+    return z, order
+
+
+def threshold_rows(g, T, V, tree, eps):
+    """Rows whose candidates sit at the threshold: with delta huge the
+    threshold is eps exactly; every child token gets probability
+    eps * (1 + U(-0.03, 0.03)) under its parent (about a third within the
+    1e-3 flag band), the rest of the mass spread over the other tokens."""
+    z = np.empty((T, V), np.float32)
+    tok = np.full(T, -1, np.int64)
+    children = [[c for c in range(1, T) if tree["parent"][c] == n] for n in range(T)]
+    for n in range(T):
+        toks = g.choice(V, max(1, len(children[n])), replace=False)
+        p = np.full(V, 0.0)
+        pc = eps * (1.0 + g.uniform(-0.03, 0.03, len(children[n])))
+        rest = 1.0 - pc.sum()
+        bg = g.random(V) + 0.5
+        bg[toks[:len(children[n])]] = 0.0
+        p += rest * bg / bg.sum()
+        for c, t, q in zip(children[n], toks, pc):
+            p[t] = q
+            tok[c] = t
+        z[n] = np.log(p).astype(np.float32)
+    return z, tok
+
+
+@pytest.mark.parametrize("name,kind", [("roofline_b16", "moderate"), ("dense341_b32", "moderate"),
+                                       ("roofline_b16", "threshold"), ("vicuna13b_b8", "threshold")])
+def test_accept_full_size_unplanted(name, kind):
+    cfg = configs.CONFIGS[name]
+    say("accept", kind, name)
+    ot = oracle_tree(cfg)
+    tree = st.build_tree(cfg)
+    B, T, V = cfg.B, ot["T"], cfg.V
+    g = np.random.default_rng(cfg.cfg_id + (11 if kind == "moderate" else 13))
+    vl = np.empty((B, T, V), np.float32)
+    tok = np.empty((B, T), np.int64)
+    delta = cfg.delta if kind == "moderate" else 1e9
+    for b in range(B):
+        if kind == "moderate":
+            vl[b], order = moderate_entropy_rows(g, T, V)
+            tok[b, 0] = g.integers(V)
+            for c in range(1, T):
+                tok[b, c] = order[ot["parent"][c], ot["rank"][c]]
+        else:
+            vl[b], tok[b] = threshold_rows(g, T, V, ot, cfg.eps)
+            tok[b, 0] = g.integers(V)
+    ref = oracle.typical_accept(vl.astype(np.float64), tok, ot, cfg.eps, delta, 1.0)
+    d_vl, d_tok = dev(vl), dev(tok.astype(np.int32))
+    o = {n: torch.empty(B, dtype=torch.int32, device="cuda") for n in ("len", "best", "next")}
+    acc = torch.empty((B, ot["depth_max"] + 1), dtype=torch.int32, device="cuda")
+    cp = torch.empty((B, T), dtype=torch.float32, device="cuda")
+    th = torch.empty((B, T), dtype=torch.float32, device="cuda")
+    mb.typical_accept(tree, d_vl, d_tok, cfg.eps, delta, 1.0, o["len"], o["best"], o["next"], acc, cp, th)
+    gpu = {"accept_len": host(o["len"]), "best": host(o["best"]), "next_tok": host(o["next"]),
+           "accepted": host(acc), "cand_p": host(cp), "row_thr": host(th)}
+    flagged = check_accept(ot, vl, tok, ref, gpu)
+    near = int((np.abs(ref["p"][:, 1:] - ref["thr"][:, 1:]) < 1e-2).sum())
+    say("  flagged decisions", flagged, "within 1e-2:", near, "of", B * (T - 1),
+        "mean accept_len", float(gpu["accept_len"].mean()))
+    if kind == "threshold":
+        assert flagged >= B * (T - 1) // 5
+    else:
+        assert near >= B * (T - 1) // 100

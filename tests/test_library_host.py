@@ -208,3 +208,33 @@ def test_workspace_sizes():
     assert mb.medusa_topk_workspace(4, 70000, 10) == 4 * 3 * 10 * 8   # three sorted lists per row
     t = mb.Tree(oracle.dense_paths(2, 2), 2, 2)
     assert mb.typical_accept_workspace(t, 3, 1000) == 3 * 3 * 1 * 32   # 3 internal rows, 1 chunk
+
+
+def test_injected_launch_failure_returns_err_hip_before_launch(monkeypatch):
+    # MEDUSA_FAULT=launch fails every launch before it is enqueued, so these
+    # argument-valid calls return ERR_HIP without touching the (fake) buffers
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    monkeypatch.setenv("MEDUSA_FAULT", "launch")
+    assert mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 64, fake, fake, fake, fake, fake) == mb.ERR_HIP
+    assert b"injected" in mb.lib.medusa_last_error()
+    assert mb.lib.medusa_topk(None, 2, 1000, 4, fake, fake, None, None, 0) == mb.ERR_HIP
+    assert mb.lib.medusa_pack_weights(None, 2, 10, 128, 1, fake, fake) == mb.ERR_HIP
+    # argument errors still win over the injected failure
+    assert mb.lib.medusa_topk(None, 2, 1000, 65, fake, fake, None, None, 0) == mb.ERR_UNSUPPORTED
+
+
+def test_trace_mode_runs_without_a_profiler():
+    # MEDUSA_TRACE=1 opens roctx at run time and wraps the call in a range; with
+    # no profiler attached the call behaves as without it (here: the injected
+    # launch failure).  A child process, since the switch is read once.
+    import subprocess
+    import sys
+    code = ("import ctypes; from tests._lib import mb; f = ctypes.c_void_p(0x1000); "
+            "s = mb.lib.medusa_heads(None, mb.BF16, 4, 1, 256, 64, f, f, f, f, f); "
+            "print(s, mb.lib.medusa_last_error().decode())")
+    env = dict(os.environ, MEDUSA_TRACE="1", MEDUSA_FAULT="launch", HIP_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", code], cwd=os.path.dirname(os.path.dirname(__file__)), env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[0] == str(mb.ERR_HIP) and "injected" in r.stdout
