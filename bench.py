@@ -283,9 +283,55 @@ def accept_sweep(cfg, args, n_seq=32):
 
 def device_info():
     import torch
+    from speculative_decoding_05_amd import binding as mb
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
-            "hbm_bytes": p.total_memory}
+    cus, clock_khz, mem_khz = mb.device_info()
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": cus,
+            "hbm_bytes": p.total_memory, "peak_clock_mhz": clock_khz / 1e3, "peak_memory_clock_mhz": mem_khz / 1e3}
+
+
+def measured_peaks(read_bytes=4 << 30, reps=5):
+    """The two roofs measured on this device in this run with the library's
+    peak kernels: a read-only stream over read_bytes (16x the last-level
+    cache), and a bf16 matrix-core loop of 4 independent 32x32x16 chains per
+    wave on 2 blocks per CU, run for ~0.1 s first so the clock settles.  Best
+    of `reps` timed calls each.  The matrix-core rate divided by the dense
+    rate per clock (1024 flop per SIMD per clock) gives the clock the matrix
+    cores would run at if they were busy every cycle."""
+    import torch
+    from speculative_decoding_05_amd import binding as mb
+    buf = torch.ones(read_bytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    fsink = torch.zeros(4, dtype=torch.float32, device="cuda")
+
+    def best_us(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, 1e3 * e0.elapsed_time(e1))
+        return best
+
+    read_us = best_us(lambda: mb.peak_hbm_read(buf, sink))
+    del buf
+    torch.cuda.empty_cache()
+    cus = mb.device_info()[0]
+    blocks, iters = 2 * cus, 2000
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.1:
+        mb.peak_mfma_bf16(blocks, iters, fsink)
+        torch.cuda.synchronize()
+    flops = mb.lib.medusa_peak_mfma_flops(blocks, iters)
+    mfma_us = best_us(lambda: mb.peak_mfma_bf16(blocks, iters, fsink))
+    mfma = flops / (mfma_us * 1e-6)
+    return {"hbm_read_gbps": read_bytes / (read_us * 1e-6) / 1e9, "hbm_read_bytes": read_bytes,
+            "mfma_bf16_tflops": mfma / 1e12, "mfma_implied_clock_ghz": mfma / (cus * 4 * 1024) / 1e9,
+            "kernels": "medusa_peak_hbm_read, medusa_peak_mfma_bf16", "reps": reps}
 
 
 def copy_rate(nbytes=1 << 30, reps=5):
@@ -361,6 +407,48 @@ def graph_variant(s, copies, steps, warmup):
     return {"us_per_step": us, "steps_per_s": 1e6 / us, "replays_match_eager": bool(match)}
 
 
+OTHER_WORKLOADS = ["roofline_b16", "vicuna13b_b8", "dense341_b32"]
+
+
+def other_workload(name, steps, warmup):
+    """Whole eager steps of another bf16 workload: inputs drawn on the device
+    (same shapes and distributions as the headline's host-drawn ones),
+    verification logits planted at the step's own candidates, per-step inputs
+    rotated past the last-level cache.  No verify pass, no oracle."""
+    import torch
+    from speculative_decoding_05_amd import configs
+    from speculative_decoding_05_amd import step as st
+    cfg = configs.CONFIGS[name]
+    tree = st.build_tree(cfg)
+    e = elem(cfg)
+    per_copy = (cfg.B * cfg.H * e + 3 * cfg.B * tree.T * cfg.nh * cfg.dh * e
+                + 2 * cfg.B * cfg.nh * cfg.L * cfg.dh * e + cfg.B * tree.T * cfg.V * 4)
+    copies = max(1, min(8, math.ceil(512 * 2 ** 20 / per_copy)))
+    inp = st.device_inputs(cfg, tree.T, seed=cfg.cfg_id)
+    s = st.Step(cfg, tree, inp, copies=copies)
+    del inp
+    torch.cuda.empty_cache()
+    s.heads()
+    s.heads_vocab()
+    s.topk_and_tokens()
+    torch.cuda.synchronize()
+    s.set_verify_logits(st.verify_logits_for(cfg, tree, s.topk_idx.cpu().numpy(), s.root.cpu().numpy()))
+    us, stage = time_steps(s, steps, warmup, copies)
+    sb, sf = stage_bytes(cfg, tree), stage_flops(cfg, tree)
+    names = list(stage)
+    roof_s = sum(max(sb[n] / HBM_PEAK, sf.get(n, 0) / BF16_PEAK) for n in names)
+    out = {"tree_steps_per_s": 1e6 / us, "seq_steps_per_s": cfg.B * 1e6 / us, "us_per_step": us,
+           "steps": steps, "input_copies": copies, "step_roofline_us": roof_s * 1e6,
+           "hbm_roofline_frac_step": roof_s / (us * 1e-6), "stage_us": stage,
+           "stage_gbps": {n: sb[n] / (stage[n] * 1e-6) / 1e9 for n in names},
+           "config": {"batch": cfg.B, "hidden": cfg.H, "attn_heads": cfg.nh, "kv_len": cfg.L,
+                      "medusa_heads": cfg.K, "tree_nodes": tree.T, "topk": cfg.k},
+           "data": "synthetic, drawn on the device (torch generator); planted verification logits"}
+    del s
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_probe(nbytes):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -392,9 +480,9 @@ def cpu_baseline(cfg, host, budget_s):
                                    host["root_tok"], configs.acc_float, cfg.k).astype(np.float64)
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle.step(args["h"], args["W1"], args["W2"], host["root_tok"], ot, cfg.k, args["q"], args["kt"],
-                    args["vt"], args["kc"], args["vc"], vl, cfg.eps, cfg.delta, cfg.temperature,
-                    round_r_bf16=rnd)
+        last = oracle.step(args["h"], args["W1"], args["W2"], host["root_tok"], ot, cfg.k, args["q"], args["kt"],
+                           args["vt"], args["kc"], args["vc"], vl, cfg.eps, cfg.delta, cfg.temperature,
+                           round_r_bf16=rnd)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 100:
@@ -406,7 +494,58 @@ def cpu_baseline(cfg, host, budget_s):
         cores = 1
     return {"value": n / el, "unit": "tree-steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} whole steps of {cfg.name} (B={cfg.B}) in float64 NumPy; "
-                      f"BLAS threads={cores}, host cpus={len(os.sched_getaffinity(0))}"}
+                      f"BLAS threads={cores}, host cpus={len(os.sched_getaffinity(0))}"}, last, vl, ot
+
+
+def step_parity(s, last, vl, ot):
+    """The GPU step on input copy 0 against the oracle step just timed (same
+    seeded inputs; the verification logits are planted at the oracle's
+    candidates and given to both): tree tokens bit-exact, and acceptance under
+    the flag rule (a decision within 1e-3 of its threshold may go either way;
+    every other decision, and the outputs as the scan of the GPU's own
+    decisions, must match)."""
+    import numpy as np
+    import torch
+    from speculative_decoding_05_amd import binding as mb
+    cfg = s.cfg
+    B, T = cfg.B, ot["T"]
+    s.heads(0)
+    s.heads_vocab(0)
+    s.topk_and_tokens(0)
+    torch.cuda.synchronize()
+    tok_g = s.tree_tok.cpu().numpy().astype(np.int64)
+    tok_o = last["tree_tok"]
+    cp = torch.empty((B, T), dtype=torch.float32, device="cuda")
+    th = torch.empty((B, T), dtype=torch.float32, device="cuda")
+    vld = torch.from_numpy(vl.astype(np.float32)).cuda()
+    tokd = torch.from_numpy(tok_o.astype(np.int32)).cuda()
+    mb.typical_accept(s.tree, vld, tokd, cfg.eps, cfg.delta, cfg.temperature, s.accept_len, s.best, s.next_tok,
+                      s.accepted, cp, th, s.ws_acc)
+    torch.cuda.synchronize()
+    ref = last["accept"]
+    p_g, thr_g = cp.cpu().numpy(), th.cpu().numpy()
+    alen, best, nxt = s.accept_len.cpu().numpy(), s.best.cpu().numpy(), s.next_tok.cpu().numpy()
+    flagged = mismatches = 0
+    for b in range(B):
+        dec = np.zeros(T, bool)
+        acc = np.zeros(T, bool)
+        acc[0] = True
+        bad = False
+        for c in range(1, T):
+            n = ot["parent"][c]
+            dec[c] = p_g[b, c] > thr_g[b, n]
+            acc[c] = acc[n] and dec[c]
+            if abs(ref["p"][b, c] - ref["thr"][b, c]) < 1e-3:
+                flagged += 1
+            elif dec[c] != ref["dec"][b, c]:
+                bad = True
+        a = int(ot["depth"][acc].max())
+        bst = int(np.flatnonzero(acc & (ot["depth"] == a))[0])
+        bad |= alen[b] != a or best[b] != bst or nxt[b] != int(np.argmax(vl[b, bst]))
+        mismatches += int(bad)
+    return {"sequences": B, "tree_tokens_equal": bool(np.array_equal(tok_g, tok_o)),
+            "decisions": B * (T - 1), "flagged_decisions": flagged, "mismatched_sequences": mismatches,
+            "accept_len_gpu": alen.tolist(), "accept_len_oracle": ref["accept_len"].tolist()}
 
 
 def main():
@@ -425,6 +564,9 @@ def main():
                     help="repetitions of each verify-pass contraction (0: skip)")
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the vocabulary projection with events on every n-th timed step")
+    ap.add_argument("--others", type=int, default=1,
+                    help="also time eager steps of the other bf16 workloads (0: skip)")
+    ap.add_argument("--peaks", type=int, default=1, help="measure the HBM-read and bf16 matrix-core peaks (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus}: only one GPU is measured; the verify tree-step has no "
@@ -556,6 +698,16 @@ def main():
     res["stage_gbps"] = {n: sb[n] / (stage_us[n] * 1e-6) / 1e9 for n in names}
     res["device"] = device_info()
     res["hbm_copy_gbps"] = copy_rate()   # device-to-device copy, read + write bytes
+    if args.peaks:
+        print("[bench] measured peaks", file=sys.stderr, flush=True)
+        pk = measured_peaks()
+        res["measured_peaks"] = pk
+        hbm_m, mfma_m = pk["hbm_read_gbps"] * 1e9, pk["mfma_bf16_tflops"] * 1e12
+        res["roofline"]["peak_measured"] = pk["hbm_read_gbps"]
+        res["roofline"]["frac_measured"] = achieved / hbm_m
+        roof_m = sum(max(sb[n] / hbm_m, sf.get(n, 0) / mfma_m) for n in names)
+        res["step_roofline_us_measured_peaks"] = roof_m * 1e6
+        res["hbm_roofline_frac_step_measured_peaks"] = roof_m / (ms_step * 1e-3)
     res["accept_len_histogram"] = accept_histogram(s, tree.depth_max)
     if args.graph:
         res["hip_graph"] = graph_variant(s, copies, args.steps, args.warmup)
@@ -566,9 +718,18 @@ def main():
           file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, host, args.cpu_seconds)
+        res["cpu_baseline"], last, vl_o, ot = cpu_baseline(cfg, host, args.cpu_seconds)
+        res["parity_vs_oracle"] = step_parity(s, last, vl_o, ot)
     else:
         res["cpu_baseline"] = None
+    if args.others and cfg.name == "vicuna7b_b1":
+        del s
+        torch.cuda.empty_cache()
+        res["other_workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            print(f"[bench] other workload {name}", file=sys.stderr, flush=True)
+            n = 40 if name == "dense341_b32" else 100
+            res["other_workloads"][name] = other_workload(name, n, 10)
     print(json.dumps(res), flush=True)
 
 

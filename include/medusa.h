@@ -380,6 +380,30 @@ medusa_status medusa_kv_commit(medusa_stream_t stream, medusa_dtype dt, const me
                                const int32_t *best_node, int32_t *seq_len, void *k_cache,
                                void *v_cache, const int32_t *next_tok, int32_t *root_tok);
 
+/* ------------------------------------------------------------------------- */
+/* (6) Achievable peaks, for the roofline the step is reported against.  The
+ *     paper summary ("实验设计与结果", roofline paragraph) places decoding on
+ *     the memory-bandwidth roof and, with many candidates, on the compute
+ *     roof; these two calls measure both roofs on the device itself, next to
+ *     the kernels they bound.
+ *  medusa_peak_hbm_read: reads `bytes` (rounded down to 16) of `buf` once,
+ *     with 16-byte non-temporal loads; time it to get the read bandwidth.
+ *     Use a buffer much larger than the 256 MB last-level cache.
+ *  medusa_peak_mfma_bf16: `blocks` blocks of 4 waves, each wave running 4
+ *     independent chains of `iters` v_mfma_f32_32x32x16_bf16 products on
+ *     register operands (no memory traffic); medusa_peak_mfma_flops(blocks,
+ *     iters) is the flop count of one call.
+ *  sink: device, 16 bytes, 16-byte aligned; never written in practice (the
+ *     results only decide a store, so the work cannot be elided).
+ *  Errors: ERR_ARG (NULL, misaligned, empty), ERR_UNSUPPORTED, ERR_HIP. */
+medusa_status medusa_peak_hbm_read(medusa_stream_t stream, const void *buf, size_t bytes, uint32_t *sink);
+medusa_status medusa_peak_mfma_bf16(medusa_stream_t stream, int blocks, int iters, float *sink);
+double medusa_peak_mfma_flops(int blocks, int iters);
+/* The current device's compute units and its peak shader and memory clocks
+ * (kHz, as the runtime reports them; 0 where not reported).  Host outputs,
+ * each may be NULL.  ERR_HIP without a device. */
+medusa_status medusa_device_info(int *compute_units, int *clock_khz, int *memory_clock_khz);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,10 @@ SIGNATURES = {
     "rejection_accept": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p]),
     "typical_accept_workspace": (_sz, [_p, _i, _i]),
     "typical_accept": (_i, [_p, _p, _i, _i, _p, _p, _f, _f, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "medusa_peak_hbm_read": (_i, [_p, _p, _sz, _p]),
+    "medusa_peak_mfma_bf16": (_i, [_p, _i, _i, _p]),
+    "medusa_peak_mfma_flops": (ctypes.c_double, [_i, _i]),
+    "medusa_device_info": (_i, [ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -419,3 +423,24 @@ def rejection_accept(tree, logits, head_logits, tree_tok, temperature, u_node, u
     check(lib.rejection_accept(_stream(), tree.handle, B, V, head_logits.shape[0], _ptr(logits), _ptr(head_logits),
                                _ptr(tree_tok), float(temperature), _ptr(u_node), _ptr(u_bonus), _ptr(accept_len),
                                _ptr(best_node), _ptr(next_tok), _ptr(accepted_tok), _ptr(keep_prob)))
+
+
+# ---------------------------------------------------------------- measurement
+def peak_hbm_read(buf, sink):
+    """Read all of `buf` (device tensor, its storage bytes) once."""
+    _dev(buf, sink)
+    check(lib.medusa_peak_hbm_read(_stream(), _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink)))
+
+
+def peak_mfma_bf16(blocks, iters, sink):
+    """One call of the bf16 matrix-core loop; returns its flop count."""
+    _dev(sink)
+    check(lib.medusa_peak_mfma_bf16(_stream(), int(blocks), int(iters), _ptr(sink)))
+    return lib.medusa_peak_mfma_flops(int(blocks), int(iters))
+
+
+def device_info():
+    """(compute units, peak clock kHz, peak memory clock kHz) of the current device."""
+    cu, ck, mk = _i(0), _i(0), _i(0)
+    check(lib.medusa_device_info(ctypes.byref(cu), ctypes.byref(ck), ctypes.byref(mk)))
+    return cu.value, ck.value, mk.value

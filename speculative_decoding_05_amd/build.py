@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmedusa_hip.so")
 SOURCES = ["host.hip", "heads.hip", "gemm.hip", "topk.hip", "attention.hip", "accept.hip", "rejection.hip", "commit.hip",
-           "debug.hip"]
+           "debug.hip", "peaks.hip"]
 # host-only C++ (no HIP headers): built with the system C++ compiler
 CXX_SOURCES = ["tree.cpp"]
 ARCH = "gfx950"

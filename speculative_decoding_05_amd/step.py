@@ -13,8 +13,11 @@ from . import binding as mb
 from . import configs, synth
 
 
-def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
-    """Upload a synth tensor: uint16 bf16 bit patterns or float32 / int32."""
+def to_device(a, device="cuda") -> torch.Tensor:
+    """Upload a synth tensor (uint16 bf16 bit patterns or float32 / int32), or
+    copy a torch tensor to `device` (always a new tensor)."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device, copy=True)
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
@@ -59,7 +62,8 @@ class Step:
                 self.W2p = mb.PackedWeights(self.W2, group)
                 torch.cuda.synchronize()
                 del self.W1, self.W2
-        self.root = to_device(host["root_tok"].astype(np.int32), dev)
+        rt = host["root_tok"]
+        self.root = to_device(rt.to(torch.int32) if isinstance(rt, torch.Tensor) else rt.astype(np.int32), dev)
         self.h = [to_device(host["h"], dev) for _ in range(copies)]
         self.q = [to_device(host["q"], dev) for _ in range(copies)]
         self.kt = [to_device(host["kt"], dev) for _ in range(copies)]
@@ -176,6 +180,25 @@ def host_inputs(cfg: configs.Config, T: int, B: int | None = None, L: int | None
     q, kt, vt = synth.tree_qkv(cfg, T, B)
     return {"W1": W1, "W2": W2, "h": synth.hidden(cfg, B), "root_tok": synth.root_tokens(cfg, B),
             "q": q, "kt": kt, "vt": vt, "kc": kc, "vc": vc}
+
+
+def device_inputs(cfg: configs.Config, T: int, seed: int = 0, device="cuda") -> dict:
+    """Inputs of the same shapes and distributions as host_inputs (weights
+    N(0, 0.02^2), activations and caches N(0, 1), rounded to the storage type;
+    uniform root tokens), drawn on the device from torch's generator: for
+    timing-only runs of the large workloads, where drawing on the host takes
+    tens of seconds."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, K, H, V, nh, dh, L = cfg.B, cfg.K, cfg.H, cfg.V, cfg.nh, cfg.dh, cfg.L
+
+    def normal(shape, std=1.0):
+        return (torch.randn(shape, generator=g, device=device) * std).to(dt)
+
+    return {"W1": normal((K, H, H), 0.02), "W2": normal((K, V, H), 0.02), "h": normal((B, H)),
+            "root_tok": torch.randint(0, V, (B,), generator=g, device=device, dtype=torch.int32),
+            "q": normal((B, T, nh, dh)), "kt": normal((B, T, nh, dh)), "vt": normal((B, T, nh, dh)),
+            "kc": normal((B, nh, L, dh)), "vc": normal((B, nh, L, dh))}
 
 
 def verify_logits_for(cfg: configs.Config, tree: mb.Tree, topk_idx: np.ndarray, root_tok: np.ndarray):

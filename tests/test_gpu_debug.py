@@ -185,3 +185,18 @@ def test_topk_tree_tokens_root_only_tree():
     mb.medusa_topk_tree_tokens(t, dev(x), k, dev(root), idx, tok)
     assert host(tok)[:, 0].tolist() == root.tolist()
     assert np.array_equal(host(idx), oracle.topk_per_head(x.astype(np.float64), k)[0])
+
+
+def test_peak_kernels_run():
+    # the two measurement kernels: they run, leave the sink alone (the data never
+    # triggers its store), and report a plausible flop count
+    buf = torch.ones(1 << 26, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    mb.peak_hbm_read(buf, sink)
+    fsink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    flops = mb.peak_mfma_bf16(8, 10, fsink)
+    torch.cuda.synchronize()
+    assert flops == 8 * 4 * 4 * 10 * 2 * 32 * 32 * 16
+    assert bool((sink == 0).all()) and bool((fsink == 0).all())
+    cus, clock_khz, _ = mb.device_info()
+    assert cus >= 1 and clock_khz >= 0

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "me
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b([a-z_]+)\s*\([^;{]*\)\s*;", text)) - {"sizeof"}
+    return set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\([^;{]*\)\s*;", text)) - {"sizeof"}
 
 
 def test_every_declared_symbol_is_exported():
