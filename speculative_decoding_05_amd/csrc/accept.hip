@@ -360,23 +360,14 @@ extern "C" size_t typical_accept_workspace(const medusa_tree *t, int B, int V) {
   return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V) * sizeof(Part);
 }
 
-extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
-                                        const float *logits, const int32_t *tree_tok, float eps,
-                                        float delta, float temperature, int32_t *accept_len,
-                                        int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
-                                        float *cand_p, float *row_thr, void *ws, size_t ws_bytes) {
-  TraceRange tr("typical_accept");
-  medusa_status s = check_tree_on_device(t);
-  if (s != MEDUSA_OK) return s;
-  if (B < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "typical_accept: B=%d V=%d", B, V);
-  if (!(eps >= 0.f) || !(delta >= 0.f) || !(temperature >= 0.f) || !isfinite(temperature))
-    return fail(MEDUSA_ERR_ARG, "typical_accept: eps, delta, temperature must be >= 0 (and finite temperature)");
-  if (!logits || !tree_tok || !accept_len || !best_node || !next_tok || !accepted_tok || !ws)
-    return fail(MEDUSA_ERR_ARG, "typical_accept: NULL pointer");
-  if (!aligned16(logits) || !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "typical_accept: logits and ws must be 16-byte aligned");
-  if (B > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "typical_accept: B=%d > 65535", B);
-  const size_t need = typical_accept_workspace(t, B, V);
-  if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
+namespace {
+
+// The checks and launches shared by typical_accept and typical_accept_noalloc;
+// `part` holds the row pass's chunk partials (B * n_internal * nchunks).
+medusa_status typical_accept_impl(const char *who, medusa_stream_t stream, const medusa_tree *t, int B, int V,
+                                  const float *logits, const int32_t *tree_tok, float eps, float delta,
+                                  float temperature, int32_t *accept_len, int32_t *best_node, int32_t *next_tok,
+                                  int32_t *accepted_tok, float *cand_p, float *row_thr, Part *part) {
   hipStream_t st = as_stream(stream);
   if (validate_enabled()) {  // NaN / +inf logits; tree tokens outside [0, V)
     ValidateSpec v;
@@ -386,22 +377,57 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
     v.tok = tree_tok;
     v.nt = (size_t)B * t->T;
     v.V = V;
-    s = validate_inputs(st, "typical_accept", v);
+    medusa_status s = validate_inputs(st, who, v);
     if (s != MEDUSA_OK) return s;
   }
   const int nchunks = chunks_for(V);
   const int greedy = temperature == 0.f;
   const float inv_tau = greedy ? 1.f : 1.f / temperature;
-  Part *part = static_cast<Part *>(ws);
   if (t->n_internal > 0) {
-    MEDUSA_LAUNCH("typical_accept", (accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
-                       logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
-    s = check_launch("typical_accept row pass");
+    MEDUSA_LAUNCH(who, (accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
+                  logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
+    medusa_status s = check_launch(who);
     if (s != MEDUSA_OK) return s;
   }
-  MEDUSA_LAUNCH("typical_accept", accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
-                     t->depth_max, t->n_internal, nchunks, t->d_slot, t->d_parent, t->d_depth, t->d_mask,
-                     eps, delta, inv_tau, greedy, part, accept_len, best_node, next_tok, accepted_tok,
-                     cand_p, row_thr);
-  return check_launch("typical_accept scan");
+  MEDUSA_LAUNCH(who, accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
+                t->depth_max, t->n_internal, nchunks, t->d_slot, t->d_parent, t->d_depth, t->d_mask,
+                eps, delta, inv_tau, greedy, part, accept_len, best_node, next_tok, accepted_tok,
+                cand_p, row_thr);
+  return check_launch(who);
+}
+
+// Arguments common to both entry points (everything but the workspace).
+medusa_status typical_accept_args(const char *who, const medusa_tree *t, int B, int V, const float *logits,
+                                  const int32_t *tree_tok, float eps, float delta, float temperature,
+                                  const int32_t *accept_len, const int32_t *best_node, const int32_t *next_tok,
+                                  const int32_t *accepted_tok) {
+  medusa_status s = check_tree_on_device(t);
+  if (s != MEDUSA_OK) return s;
+  if (B < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "%s: B=%d V=%d", who, B, V);
+  if (!(eps >= 0.f) || !(delta >= 0.f) || !(temperature >= 0.f) || !isfinite(temperature))
+    return fail(MEDUSA_ERR_ARG, "%s: eps, delta, temperature must be >= 0 (and finite temperature)", who);
+  if (!logits || !tree_tok || !accept_len || !best_node || !next_tok || !accepted_tok)
+    return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
+  if (!aligned16(logits)) return fail(MEDUSA_ERR_ARG, "%s: logits must be 16-byte aligned", who);
+  if (B > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: B=%d > 65535", who, B);
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
+extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
+                                        const float *logits, const int32_t *tree_tok, float eps,
+                                        float delta, float temperature, int32_t *accept_len,
+                                        int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
+                                        float *cand_p, float *row_thr, void *ws, size_t ws_bytes) {
+  TraceRange tr("typical_accept");
+  medusa_status s = typical_accept_args("typical_accept", t, B, V, logits, tree_tok, eps, delta, temperature,
+                                        accept_len, best_node, next_tok, accepted_tok);
+  if (s != MEDUSA_OK) return s;
+  if (!ws) return fail(MEDUSA_ERR_ARG, "typical_accept: NULL workspace");
+  if (!aligned16(ws)) return fail(MEDUSA_ERR_ARG, "typical_accept: ws must be 16-byte aligned");
+  const size_t need = typical_accept_workspace(t, B, V);
+  if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
+  return typical_accept_impl("typical_accept", stream, t, B, V, logits, tree_tok, eps, delta, temperature,
+                             accept_len, best_node, next_tok, accepted_tok, cand_p, row_thr, static_cast<Part *>(ws));
 }
