@@ -330,6 +330,21 @@ medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B
                              int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
                              float *cand_p, float *row_thr, void *ws, size_t ws_bytes);
 
+/* typical_accept without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (minus ws / ws_bytes) and results as
+ * typical_accept (bit-identical: the same kernels).  The row pass's partials
+ * go to a 4 MiB array the library keeps in each GPU's memory for the life of
+ * the process (looked up on the first call on a device); the call allocates
+ * nothing.  Limit: B * (number of tree nodes with children) * ceil(V / 4096)
+ * <= 131072, else MEDUSA_ERR_UNSUPPORTED with nothing enqueued.  All calls on
+ * one GPU share that array: calls that may overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller. */
+medusa_status typical_accept_noalloc(medusa_stream_t stream, const medusa_tree *t, int B, int V,
+                                     const float *logits, const int32_t *tree_tok, float eps, float delta,
+                                     float temperature, int32_t *accept_len, int32_t *best_node,
+                                     int32_t *next_tok, int32_t *accepted_tok, float *cand_p, float *row_thr);
+
 /* (4b) Rejection-sampling acceptance, the rule typical acceptance replaces
  *     (paper summary, "两个扩展" and "关键发现"; the pages name it without
  *     spelling it out).  Starting at the root (always kept), the children of

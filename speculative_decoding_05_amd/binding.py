@@ -69,6 +69,7 @@ SIGNATURES = {
     "rejection_accept": (_i, [_p, _p, _i, _i, _i, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p, _p]),
     "typical_accept_workspace": (_sz, [_p, _i, _i]),
     "typical_accept": (_i, [_p, _p, _i, _i, _p, _p, _f, _f, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
+    "typical_accept_noalloc": (_i, [_p, _p, _i, _i, _p, _p, _f, _f, _f, _p, _p, _p, _p, _p, _p]),
     "medusa_peak_hbm_read": (_i, [_p, _p, _sz, _p]),
     "medusa_peak_mfma_bf16": (_i, [_p, _i, _i, _p]),
     "medusa_peak_mfma_flops": (ctypes.c_double, [_i, _i]),
@@ -412,6 +413,16 @@ def typical_accept(tree, logits, tree_tok, eps, delta, temperature, accept_len, 
                              float(delta), float(temperature), _ptr(accept_len), _ptr(best_node),
                              _ptr(next_tok), _ptr(accepted_tok), _ptr(cand_p), _ptr(row_thr), _ptr(ws),
                              ws.numel()))
+
+
+def typical_accept_noalloc(tree, logits, tree_tok, eps, delta, temperature, accept_len, best_node, next_tok,
+                           accepted_tok, cand_p=None, row_thr=None):
+    """typical_accept with the library's own scratch (no workspace argument)."""
+    _dev(logits, tree_tok, accept_len, best_node, next_tok, accepted_tok, cand_p, row_thr)
+    B, T, V = logits.shape
+    check(lib.typical_accept_noalloc(_stream(), tree.handle, B, V, _ptr(logits), _ptr(tree_tok), float(eps),
+                                     float(delta), float(temperature), _ptr(accept_len), _ptr(best_node),
+                                     _ptr(next_tok), _ptr(accepted_tok), _ptr(cand_p), _ptr(row_thr)))
 
 
 def rejection_accept(tree, logits, head_logits, tree_tok, temperature, u_node, u_bonus, accept_len, best_node,

@@ -15,6 +15,8 @@
 // next greedy token from its row.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace medusa;
@@ -355,6 +357,41 @@ inline int chunks_for(int V) { return (V + kThreads * kVec * 4 - 1) / (kThreads 
 
 }  // namespace
 
+// Scratch of typical_accept_noalloc: the row pass's chunk partials, in device
+// memory the library owns for the life of the process (one copy per GPU).
+// 131072 partials of 32 bytes = 4 MiB: B * internal nodes * ceil(V / 4096)
+// must not exceed that (the 341-node dense tree at batch 32 and V = 32000
+// needs 21760).  Host code never uses this name as an address: it looks the
+// device address up once per device (scratch_on_device below).
+constexpr size_t kScratchParts = 131072;
+static __device__ __align__(256) Part scratch[kScratchParts];
+
+namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+Part *g_scratch_ptr[kScratchDevices] = {};
+
+// The current device's copy of `scratch` (hipGetSymbolAddress on the first
+// call on each device, with that device current).
+medusa_status scratch_on_device(const char *who, Part **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+    return fail(MEDUSA_ERR_HIP, "%s: no usable HIP device", who);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MEDUSA_ERR_HIP, "%s: device address of the scratch array: %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<Part *>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MEDUSA_OK;
+}
+
+}  // namespace
+
 extern "C" size_t typical_accept_workspace(const medusa_tree *t, int B, int V) {
   if (!t || B < 1 || V < 1) return 0;
   return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V) * sizeof(Part);
@@ -430,4 +467,28 @@ extern "C" medusa_status typical_accept(medusa_stream_t stream, const medusa_tre
   if (ws_bytes < need) return fail(MEDUSA_ERR_WORKSPACE, "typical_accept: workspace %zu < %zu", ws_bytes, need);
   return typical_accept_impl("typical_accept", stream, t, B, V, logits, tree_tok, eps, delta, temperature,
                              accept_len, best_node, next_tok, accepted_tok, cand_p, row_thr, static_cast<Part *>(ws));
+}
+
+extern "C" medusa_status typical_accept_noalloc(medusa_stream_t stream, const medusa_tree *t, int B, int V,
+                                                const float *logits, const int32_t *tree_tok, float eps,
+                                                float delta, float temperature, int32_t *accept_len,
+                                                int32_t *best_node, int32_t *next_tok, int32_t *accepted_tok,
+                                                float *cand_p, float *row_thr) {
+  TraceRange tr("typical_accept_noalloc");
+  const char *who = "typical_accept_noalloc";
+  medusa_status s = typical_accept_args(who, t, B, V, logits, tree_tok, eps, delta, temperature, accept_len,
+                                        best_node, next_tok, accepted_tok);
+  if (s != MEDUSA_OK) return s;
+  const size_t need = (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V);
+  if (need > kScratchParts)
+    return fail(MEDUSA_ERR_UNSUPPORTED,
+                "%s: B * internal nodes * ceil(V/4096) = %zu partials exceed the %zu of the library's scratch",
+                who, need, kScratchParts);
+  Part *part = nullptr;
+  s = scratch_on_device(who, &part);
+  if (s != MEDUSA_OK) return s;
+  // every partial the scan reads is written by the row pass of the same call,
+  // so nothing needs clearing
+  return typical_accept_impl(who, stream, t, B, V, logits, tree_tok, eps, delta, temperature, accept_len,
+                             best_node, next_tok, accepted_tok, cand_p, row_thr, part);
 }
