@@ -554,6 +554,314 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Wide tree attention (bf16, dh = 128, 64 < T <= 384): one block per (b, head,
+// prefix slice) with NW waves of 32 queries that together cover every tree
+// node, so each prefix key is read from HBM once per (b, head) and staged once
+// in LDS for all of them.  Scores are computed transposed on
+// v_mfma_f32_32x32x16_bf16 (each lane owns one query and 16 of every 32 keys;
+// the other 16 sit in lane ^ 32, one permlane32 swap away), and O^T += V^T P^T
+// takes V^T straight from the row-major tile through the LDS transpose read.
+// K/V tiles of 64 keys go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i's 16 bytes land at the wave's base + 16 i)
+// in three stages, the loads of tile t+2 issued while tile t is worked on, one
+// barrier per tile.  The 16-byte chunks of each 256-byte row are XOR-swizzled
+// (K: chunk ^ (row & 15), V: chunk ^ 2 (row & 3)) so that the 16 rows of a
+// b128 K read and the 4 rows x 32 bytes of a 16-lane transpose read hit
+// distinct banks; the loads apply the swizzle on the global side (lane i of a
+// load fills physical chunk i % 16 and fetches the logical chunk that maps
+// there), and a fragment's address is the lane's base XOR the step's offset.
+// The tree mask rows of the block's nodes are copied to LDS once.  The
+// softmax keeps a per-query reference maximum and re-references it (and
+// rescales O) only when a score exceeds it by more than 2^8, so the common
+// path per score is a third of a max3, one FMA, one exp2 and one add.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kWideQ = 32;                 // queries per wave
+constexpr int kWideStageVec = 2048;        // one stage: K (1024) then V (1024) 16-byte chunks, 64 keys x 128 dh each
+constexpr int kWideMaskMax = 384 * 6;      // mask words of a 384-node tree
+constexpr float kLazyRescale = 8.f;        // log2 headroom before the reference maximum moves
+
+__shared__ u32x4_t wide_stage0[kWideStageVec];
+__shared__ u32x4_t wide_stage1[kWideStageVec];
+__shared__ u32x4_t wide_stage2[kWideStageVec];
+__shared__ uint64_t wide_mask[kWideMaskMax];
+
+template <int S>
+__device__ __forceinline__ u32x4_t *wide_stage() {
+  if (S == 0) return wide_stage0;
+  if (S == 1) return wide_stage1;
+  return wide_stage2;
+}
+
+// s_waitcnt with vmcnt = vm and lgkmcnt = lgkm (gfx9 encoding; expcnt left at its maximum)
+#define ATT_WAITCNT(vm, lgkm) \
+  __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | ((((vm) >> 4) & 3) << 14) | (7 << 4) | (((lgkm) & 0xF) << 8))
+
+__device__ __forceinline__ void lds_dma16(const uint16_t *g, u32x4_t *l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)g,
+                                   (void __attribute__((address_space(3))) *)l, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wide_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+
+// max of x over lanes l and l ^ 32 (in every lane), without LDS: permlane32
+// swap exchanges the two 32-lane halves between its two results, so together
+// with x they cover x[l] and x[l ^ 32]
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(x, fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
+    int B, int nh, int T, int W, int L, int Lstride, const int32_t *__restrict__ seq_len, float scale_log2,
+    int nsplit, int per_split, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kt,
+    const uint16_t *__restrict__ vt, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    const uint64_t *__restrict__ mask, const uint32_t *__restrict__ tile_need, uint16_t *__restrict__ out,
+    float *__restrict__ ws_o, float2 *__restrict__ ws_ml) {
+  constexpr int DH = 128;
+  constexpr int KS = DH / 16;          // 16-deep steps of the score product
+  constexpr int DT = DH / 32;          // 32-wide output tiles
+  constexpr int LW = NW < 8 ? NW : 8;  // waves that issue the tile loads
+  constexpr int IPW = 16 / LW;         // 1 KiB K loads (and as many V loads) per loader wave per tile
+  const int split = blockIdx.x % nsplit;
+  const int bh = blockIdx.x / nsplit;
+  const int h = bh % nh, b = bh / nh;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS bases stay scalar
+  const int lane = threadIdx.x & 63;
+  const int lq = lane & 31, hh = lane >> 5;
+  const int tq = wave * kWideQ + lq;  // this lane's query (tree node)
+  const bool qvalid = tq < T;
+  const bool wave_live = wave * kWideQ < T;
+
+  // Q^T as the B operand of step k: q[tq][16k + 8hh .. +8]
+  u32x4_t qreg[KS];
+  {
+    const uint16_t *qp = q + (((size_t)b * T + (qvalid ? tq : 0)) * nh + h) * DH + hh * 8;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      qreg[k] = qvalid ? *reinterpret_cast<const u32x4_t *>(qp + k * 16) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // the tree's mask rows, visible to all waves after the first barrier below
+  for (int i = threadIdx.x; i < T * W; i += 64 * NW) wide_mask[i] = mask[i];
+  ATT_WAITCNT(0, 15);  // nothing but the tile loads is outstanding from here on
+
+  // keys: prefix slice [c0, c1) of this sequence's Lb cached keys, then (last
+  // slice) the tree tiles that hold an ancestor of some node; a wave skips
+  // the tree tiles none of its 32 nodes needs
+  const int Lb = seq_len ? min(max(seq_len[b], 0), L) : L;
+  const int c0 = split * per_split;
+  const int c1 = min(Lb, c0 + per_split);
+  const int ncache = c1 > c0 ? (c1 - c0 + kKT - 1) / kKT : 0;
+  uint32_t need_block = 0u, need_wave = 0u;
+  const int ngroups = (T + 15) / 16;
+  for (int g = 0; g < ngroups; ++g) {
+    const uint32_t nb = tile_need[g];
+    need_block |= nb;
+    if ((g >> 1) == wave) need_wave |= nb;
+  }
+  const int ntree = split == nsplit - 1 ? __builtin_popcount(need_block) : 0;
+  const int ntiles = ncache + ntree;
+  auto tree_tile = [&](int i) __attribute__((always_inline)) {  // i-th needed tree tile
+    uint32_t m = need_block;
+    for (int j = 0; j < i; ++j) m &= m - 1;
+    return __builtin_ctz(m);
+  };
+
+  const uint16_t *kc_bh = kc + ((size_t)b * nh + h) * Lstride * DH;
+  const uint16_t *vc_bh = vc + ((size_t)b * nh + h) * Lstride * DH;
+  const uint16_t *kt_b = kt + ((size_t)b * T * nh + h) * DH;
+  const uint16_t *vt_b = vt + ((size_t)b * T * nh + h) * DH;
+
+  // load `ins` (< 16) of a loader wave fills K rows 4 ins .. 4 ins + 3 (V the
+  // same, 16 KiB further on); lane i fills physical chunk i % 16 of row
+  // 4 ins + i / 16 and fetches the logical chunk stored there
+  auto issue = [&](int tile, u32x4_t *stg) __attribute__((always_inline)) {
+    if (wave >= LW) return;
+    const bool is_tree = tile >= ncache;
+    const int r0 = is_tree ? tree_tile(tile - ncache) * kKT : c0 + tile * kKT;
+    const int rend = is_tree ? T : c1;
+    const long stride = is_tree ? (long)nh * DH : (long)DH;
+    const uint16_t *kb = is_tree ? kt_b : kc_bh;
+    const uint16_t *vb = is_tree ? vt_b : vc_bh;
+    const int cv = (lane & 15) ^ ((lane >> 4) << 1);  // row & 3 == lane / 16
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int ins = IPW * wave + j;
+      const int r = 4 * ins + (lane >> 4);
+      const int row = min(r0 + r, rend - 1);  // past the end: a valid row whose scores are masked
+      const int ck = (lane & 15) ^ (r & 15);
+      lds_dma16(kb + row * stride + ck * 8, stg + ins * 64);
+      lds_dma16(vb + row * stride + cv * 8, stg + 1024 + ins * 64);
+    }
+  };
+
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  float m_ref = -INFINITY, l_lane = 0.f;
+  // per-lane LDS byte addresses.  K fragment of step k: row 32 st + lq,
+  // logical chunk 2k + hh, physical (2k + hh) ^ (lq & 15) = base ^ 2k (the
+  // step only flips bits 5-7 of the byte address).  V^T read by 16-lane group
+  // g: rows 32 st + 16 ks + 4 (g >> 1) + (li >> 2) (+8), logical chunk
+  // 4 d + 2 (g & 1) + (li & 3) / 2, physical that ^ 2 (li >> 2) = base ^ 4d.
+  const int g = lane >> 4, li = lane & 15;
+  const int kaddr = lq * 256 + ((hh ^ (lq & 1)) | (((lq & 15) >> 1) << 1)) * 16;
+  const int vaddr = 16384 + (4 * (g >> 1) + (li >> 2)) * 256 +
+                    ((2 * (g & 1) + ((li & 3) >> 1)) ^ ((li >> 2) << 1)) * 16 + (li & 1) * 8;
+
+  auto consume = [&](int tile, const u32x4_t *stg) __attribute__((always_inline)) {
+    if (!wave_live) return;
+    const bool is_tree = tile >= ncache;
+    const int tt = is_tree ? tree_tile(tile - ncache) : 0;
+    if (is_tree && !((need_wave >> tt) & 1u)) return;
+    const int kend = is_tree ? T - tt * kKT : c1 - (c0 + tile * kKT);
+    const bool masked = is_tree || kend < kKT;
+    const char *base = reinterpret_cast<const char *>(stg);
+#pragma unroll 1
+    for (int st = 0; st < 2; ++st) {  // 32-key halves of the tile (not unrolled: register budget)
+      // S^T: lane holds S[key 32 st + 8 j + 4 hh + i][tq] in s[4 j + i]
+      f32x16_t s;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = 0.f;
+      const char *kp = base + st * 32 * 256;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) s = mfma32(*reinterpret_cast<const u32x4_t *>(kp + (kaddr ^ (k << 5))), qreg[k], s);
+      if (masked) {
+        const uint64_t mw = is_tree ? (qvalid ? wide_mask[tq * W + tt] : 0ull) : ~0ull;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = st * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const bool ok = key < kend && ((mw >> key) & 1ull);
+          s[e] = ok ? s[e] : -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+      for (int e = 3; e < 15; e += 2) mx = fmaxf(fmaxf(mx, s[e]), s[e + 1]);
+      mx = fmaxf(mx, s[15]);
+      mx = xor32_max(mx);
+      const float m_cand = mx * scale_log2;
+      const bool move = m_cand > m_ref + kLazyRescale;
+      if (__any(move)) {  // rare after the first keys: re-reference and rescale
+        const float m_new = move ? m_cand : m_ref;
+        const float alpha = m_new == m_ref ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+        for (int d = 0; d < DT; ++d) oacc[d] *= alpha;
+        l_lane *= alpha;
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -m_use));
+        ps += s[e];
+      }
+      l_lane += ps;
+      // P^T B operand of 16-key step ks: slot 8 hh + e is key 16 ks + 8 (e >> 2) + 4 hh + (e & 3),
+      // i.e. this lane's own s[8 ks .. 8 ks + 7]
+      u32x4_t pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pb[ks] = u32x4_t{pack2(s[8 * ks], s[8 * ks + 1]), pack2(s[8 * ks + 2], s[8 * ks + 3]),
+                         pack2(s[8 * ks + 4], s[8 * ks + 5]), pack2(s[8 * ks + 6], s[8 * ks + 7])};
+      // O^T += V^T P^T: lane i of group g receives V[row .. row + 3][column + i]
+      const char *vp = base + st * 32 * 256;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const int va = vaddr ^ (64 * d);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint2 lo = read_tr(reinterpret_cast<const uint16_t *>(vp + va + 16 * ks * 256));
+          const uint2 hi = read_tr(reinterpret_cast<const uint16_t *>(vp + va + (16 * ks + 8) * 256));
+          oacc[d] = mfma32(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[ks], oacc[d]);
+        }
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    // tile t lives in stage t % 3; its loads are issued two tiles ahead (past
+    // the end the last tile is re-loaded into a stage nobody reads again)
+    issue(0, wide_stage<0>());
+    issue(min(1, ntiles - 1), wide_stage<1>());
+    auto body = [&](int t, const u32x4_t *cur, u32x4_t *dst, bool issue_first) __attribute__((always_inline)) {
+      ATT_WAITCNT(2 * IPW, 15);  // this wave's loads of tile t are in LDS (tile t+1's may still fly)
+      wide_barrier();            // everyone's are, and everyone finished tile t-1 (the stage of t+2)
+      if (issue_first) issue(min(t + 2, ntiles - 1), dst);
+      consume(t, cur);
+      if (!issue_first) issue(min(t + 2, ntiles - 1), dst);
+    };
+    // (the first body of each round issues after its compute: the compiler's
+    // wait insertion cannot separate the stages at the loop head and would
+    // otherwise wait for the loads it has just issued)
+    for (int t = 0; t < ntiles; t += 3) {
+      body(t, wide_stage<0>(), wide_stage<2>(), false);
+      if (t + 1 < ntiles) body(t + 1, wide_stage<1>(), wide_stage<0>(), true);
+      if (t + 2 < ntiles) body(t + 2, wide_stage<2>(), wide_stage<1>(), true);
+    }
+    ATT_WAITCNT(0, 15);  // the re-loads past the end land before the block's LDS is handed on
+  }
+
+  const float l_tot = l_lane + __shfl_xor(l_lane, 32);
+  if (!qvalid) return;
+  // lane holds O^T[32 d + 8 j + 4 hh + i][tq] in oacc[d][4 j + i]
+  if (nsplit == 1) {
+    const float inv = 1.f / l_tot;
+    uint16_t *op = out + (((size_t)b * T + tq) * nh + h) * DH + 4 * hh;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 w;
+        w.x = pack2(oacc[d][4 * j] * inv, oacc[d][4 * j + 1] * inv);
+        w.y = pack2(oacc[d][4 * j + 2] * inv, oacc[d][4 * j + 3] * inv);
+        *reinterpret_cast<uint2 *>(op + 32 * d + 8 * j) = w;
+      }
+  } else {
+    const size_t row = (((size_t)split * B + b) * nh + h) * T + tq;
+    float *op = ws_o + row * DH + 4 * hh;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4 *>(op + 32 * d + 8 * j) =
+            make_float4(oacc[d][4 * j], oacc[d][4 * j + 1], oacc[d][4 * j + 2], oacc[d][4 * j + 3]);
+    if (hh == 0) ws_ml[row] = make_float2(m_ref, l_tot);
+  }
+}
+
+// The wide kernel serves dh = 128 trees of 65..384 tokens.
+inline bool use_wide(medusa_dtype dt, int dh, int T) { return dt == MEDUSA_BF16 && dh == 128 && T > kQB && T <= 384; }
+inline int wide_waves(int T) { return T <= 128 ? 4 : T <= 256 ? 8 : 12; }
+
+// One block per (b, head) already fills the chip from one block per CU; with
+// fewer pairs the prefix is split (slices of at least 256 keys) until there
+// are about as many blocks as CUs.
+inline Split choose_split_wide(int B, int nh, int L) {
+  const long pairs = (long)B * nh;
+  const long cus = device_compute_units();
+  int ns = pairs >= cus ? 1 : (int)((cus + pairs - 1) / pairs);
+  const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
+  if (ns > max_ns) ns = max_ns;
+  return split_into(L, ns);
+}
+
 // Cache layout [B][nh][Lstride][dh]; sequence b attends to its first
 // seq_len[b] cached keys (all L when seq_len is NULL), clamped to [0, L].
 struct Prefix {
@@ -600,6 +908,40 @@ medusa_status launch_bf16(hipStream_t st, const medusa_tree *t, int B, int nh, P
   return check_launch("tree_attention merge");
 }
 
+
+template <int NW>
+medusa_status launch_wide(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, Split sp, float scale,
+                          const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
+                          const void *v_cache, void *out, void *ws) {
+  constexpr int DH = 128;
+  const long nblocks = (long)B * nh * sp.nsplit;
+  if (nblocks > 0x7fffffffL) return fail(MEDUSA_ERR_UNSUPPORTED, "tree_attention: grid too large");
+  float *ws_o = nullptr;
+  float2 *ws_ml = nullptr;
+  if (sp.nsplit > 1) {
+    ws_o = static_cast<float *>(ws);
+    ws_ml = reinterpret_cast<float2 *>(ws_o + (size_t)sp.nsplit * B * nh * t->T * DH);
+  }
+  MEDUSA_LAUNCH("tree_attention", tree_attn_wide_bf16<NW>, dim3((unsigned)nblocks), dim3(64 * NW), 0, st, B, nh,
+                t->T, t->W, pf.L, pf.Lstride, pf.seq_len, scale * kLog2e, sp.nsplit, sp.per_split,
+                static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k_tree),
+                static_cast<const uint16_t *>(v_tree), static_cast<const uint16_t *>(k_cache),
+                static_cast<const uint16_t *>(v_cache), t->d_mask, t->d_tile_need, static_cast<uint16_t *>(out),
+                ws_o, ws_ml);
+  medusa_status s = check_launch("tree_attention");
+  if (s != MEDUSA_OK || sp.nsplit == 1) return s;
+  const long rows = (long)B * nh * t->T;
+  const int rpb = 256 / (DH / 4);
+  auto merge = sp.nsplit == 2 ? tree_attn_merge_bf16<DH, 2>
+             : sp.nsplit == 3 ? tree_attn_merge_bf16<DH, 3>
+             : sp.nsplit == 4 ? tree_attn_merge_bf16<DH, 4>
+             : sp.nsplit <= kMergeUnroll ? tree_attn_merge_bf16<DH, kMergeUnroll>
+                                         : tree_attn_merge_bf16<DH, 0>;
+  MEDUSA_LAUNCH("tree_attention", merge, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, st,
+                B, nh, t->T, sp.nsplit, ws_o, ws_ml, static_cast<uint16_t *>(out));
+  return check_launch("tree_attention merge");
+}
+
 template <int DH>
 medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, Prefix pf, float scale,
                          const void *q, const void *k_tree, const void *v_tree, const void *k_cache,
@@ -617,7 +959,7 @@ medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, Pr
 extern "C" size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t, int B, int nh,
                                            int dh, int L) {
   if (!t || B < 1 || nh < 1 || dh < 1 || L < 0 || dt != MEDUSA_BF16) return 0;
-  const Split sp = choose_split(B, nh, t->T, L);
+  const Split sp = use_wide(dt, dh, t->T) ? choose_split_wide(B, nh, L) : choose_split(B, nh, t->T, L);
   if (sp.nsplit == 1) return 0;
   return (size_t)sp.nsplit * B * nh * t->T * (dh + 2) * sizeof(float);
 }
@@ -647,6 +989,13 @@ medusa_status attention_entry(const char *who, medusa_stream_t stream, medusa_dt
   if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)dh) : scale;
   hipStream_t st = as_stream(stream);
+  if (use_wide(dt, dh, t->T)) {
+    const Split sp = choose_split_wide(B, nh, L);
+    const int nw = wide_waves(t->T);
+    return nw == 4 ? launch_wide<4>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+         : nw == 8 ? launch_wide<8>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)
+                   : launch_wide<12>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws);
+  }
   if (dt == MEDUSA_BF16) {
     const bool two = qtiles_for(t->T) == 2;
     const Split sp = choose_split(B, nh, t->T, L);

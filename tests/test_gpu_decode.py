@@ -53,12 +53,15 @@ def test_ragged_attention_three_blocks_per_cu():
 
 @pytest.mark.parametrize("dtype,paths,dh,L_cap,lens", [
     ("bf16", "greedy64", 128, 700, [0, 64, 300, 651, 700]),   # several prefix slices
+    ("bf16", "dense44", 128, 1100, [0, 333, 1100]),           # 341 nodes: the wide kernel, 4 slices
     ("bf16", "dense22", 64, 90, [5, 0, 90]),
     ("f32", "dense22", 64, 140, [0, 77, 129]),
 ])
 def test_ragged_attention_parity(dtype, paths, dh, L_cap, lens):
     if paths == "greedy64":
         p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10
+    elif paths == "dense44":
+        p, K, k = oracle.dense_paths(4, 4), 4, 4
     else:
         p, K, k = oracle.dense_paths(2, 2), 2, 2
     ot = oracle.build_tree(p, K, k)

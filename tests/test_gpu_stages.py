@@ -369,6 +369,55 @@ def test_attention_parity(dtype, tree, B, nh, dh, L):
     check_attn(dtype, got, ref)
 
 
+# The wide kernel (bf16, dh = 128, 65..384 tree tokens): one block per
+# (b, head), 4 / 8 / 12 waves of 32 nodes; prefix slices and the merge when
+# the (b, head) pairs are fewer than the CUs.
+@pytest.mark.parametrize("tree,B,nh,L", [
+    ("dense34", 2, 2, 300),      # T = 85: 4 waves, ragged last cache tile (300 = 4 x 64 + 44)
+    ("greedy128", 1, 3, 1000),   # T = 128: 4 waves, 3 prefix slices + merge
+    ("greedy256", 1, 4, 1000),   # T = 256: 8 waves, 3 prefix slices
+    ("dense36", 2, 2, 64),       # T = 259: 12 waves, one cache tile
+    ("dense44", 1, 2, 2048),     # T = 341: 12 waves, 8 prefix slices + merge
+    ("dense44", 2, 1, 0),        # T = 341, empty prefix: tree keys only
+    ("dense44", 1, 1, 1),        # T = 341, one cached key
+])
+def test_attention_wide_parity(tree, B, nh, L):
+    say("attention (wide)", tree, B, nh, L)
+    spec = {"dense34": (oracle.dense_paths(3, 4), 3, 4), "dense36": (oracle.dense_paths(3, 6), 3, 6),
+            "dense44": (oracle.dense_paths(4, 4), 4, 4),
+            "greedy128": (oracle.greedy_paths(configs.acc_exact, 4, 127, 10), 4, 10),
+            "greedy256": (oracle.greedy_paths(configs.acc_exact, 4, 255, 10), 4, 10)}[tree]
+    ot, t, q, kt, vt, kc, vc = attn_case("bf16", *spec, B, nh, 128, L, seed=7 * B + L)
+    got = run_attn("bf16", t, q, kt, vt, kc, vc)
+    f = synth.as_f64
+    check_attn("bf16", got, oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot))
+
+
+def test_attention_wide_non_ancestors_do_not_leak_bitwise():
+    # the 341-node tree: perturbing the K/V of every node outside a node's
+    # branch leaves that node's output bitwise unchanged
+    paths = oracle.dense_paths(4, 4)
+    ot, t, q, kt, vt, kc, vc = attn_case("bf16", paths, 4, 4, 1, 2, 128, 200, 17)
+    base = run_attn("bf16", t, q, kt, vt, kc, vc)
+    for j in (0, 7, 100, ot["T"] - 1):
+        anc = set(oracle.ancestors(ot, j))
+        kt2, vt2 = kt.copy(), vt.copy()
+        others = [i for i in range(ot["T"]) if i not in anc]
+        kt2[:, others] = store(np.full(kt2[:, others].shape, 3.0, np.float32), "bf16")
+        vt2[:, others] = store(np.full(vt2[:, others].shape, -2.0, np.float32), "bf16")
+        pert = run_attn("bf16", t, q, kt2, vt2, kc, vc)
+        assert np.array_equal(pert[:, j], base[:, j]), j
+
+
+def test_attention_wide_deterministic_and_peaked():
+    ot, t, q, kt, vt, kc, vc = attn_case("bf16", oracle.dense_paths(4, 4), 4, 4, 2, 2, 128, 700, 19, qscale=4.0)
+    a = run_attn("bf16", t, q, kt, vt, kc, vc)
+    b = run_attn("bf16", t, q, kt, vt, kc, vc)
+    assert np.array_equal(a, b)
+    f = synth.as_f64
+    check_attn("bf16", a, oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot))
+
+
 def test_attention_peaked_scores():
     ot, t, q, kt, vt, kc, vc = attn_case("bf16", oracle.dense_paths(3, 2), 3, 2, 1, 2, 128, 300, 5, qscale=4.0)
     got = run_attn("bf16", t, q, kt, vt, kc, vc)
