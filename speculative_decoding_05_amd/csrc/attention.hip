@@ -846,7 +846,6 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
   }
 }
 
-// The wide kernel serves dh = 128 trees of 65..384 tokens.
 // The wide kernel serves dh = 128 trees of 65..384 tokens.  (Measured on
 // MI355X at batch 1 with the 64-node tree: two waves per block over 8 prefix
 // slices are slower than the 64-query kernel, 14.6 + 4.4 against 13.9 + 4.4 us.)
