@@ -70,6 +70,9 @@ struct Split {
 // Prefix slices per (b, head): measured on MI355X, split partials plus the
 // merge cost more than they gain once there are >= 128 (b, head, query-group)
 // blocks, so the prefix is split only below that (down to 256 keys a slice).
+// With 32 or fewer blocks before splitting (one sequence's heads) the split
+// aims at one block per CU instead, down to 128 keys a slice (batch 1, 32
+// heads, 1024 keys: 8 slices, kernel + merge 16.2 us against 17.4 with 4).
 // Query tiles per wave: two once the tree has more than 64 tokens.
 inline int qtiles_for(int T) { return T > kQB ? 2 : 1; }
 
@@ -86,7 +89,9 @@ inline Split split_into(int L, int ns) {
 inline Split choose_split(int B, int nh, int T, int L) {
   const int qb = kQB * qtiles_for(T);
   const long pairs = (long)B * nh * ((T + qb - 1) / qb);
-  int ns = (int)((kSplitTargetBlocks + pairs - 1) / pairs);
+  const long cus = device_compute_units();
+  const bool few = pairs <= 32;
+  int ns = (int)(((few ? cus : kSplitTargetBlocks) + pairs - 1) / pairs);
   // Between one and two (b, head) pairs per CU the CUs that get two set the
   // time.  With one query tile per wave the kernel also builds in 168
   // registers, which runs three blocks per CU: two slices then fill
@@ -95,13 +100,14 @@ inline Split choose_split(int B, int nh, int T, int L) {
   // with the merge; three slices at two blocks per CU before).  Elsewhere the
   // 168-register build is slower (batch 1: 16.2 -> 17.5 us).
   bool three = false;
-  const long cus = device_compute_units();
   if (pairs > cus && pairs < 2 * cus) {
     three = qtiles_for(T) == 1;
     ns = three ? 2 : 3;
   }
-  const int max_ns = L / kMinKeysPerSplit > 1 ? L / kMinKeysPerSplit : 1;
+  const int min_keys = few ? kMinKeysPerSplit / 2 : kMinKeysPerSplit;
+  const int max_ns = L / min_keys > 1 ? L / min_keys : 1;
   if (ns > max_ns) ns = max_ns;
+  if (ns > kMergeUnroll) ns = kMergeUnroll;
   Split sp = split_into(L, ns);
   sp.three_per_cu = three;
   return sp;

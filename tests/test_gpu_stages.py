@@ -369,6 +369,50 @@ def test_attention_parity(dtype, tree, B, nh, dh, L):
     check_attn(dtype, got, ref)
 
 
+# Small batches (bf16, dh = 128, trees of up to 64 nodes, few (b, head)
+# pairs): the prefix is cut into slices merged by the second kernel.
+@pytest.mark.parametrize("tree,B,nh,L", [
+    ("greedy64", 1, 2, 4000),    # 8 slices of 512 keys
+    ("greedy40", 1, 3, 1000),    # T = 41: a partial query tile; 6 slices of 192 keys, the last 40
+    ("dense32", 1, 32, 1024),    # 32 pairs (the 7B heads at batch 1), T = 15: 8 slices of 128 keys
+    ("greedy64", 7, 32, 513),    # 224 pairs: no split
+    ("chain5", 2, 1, 17),        # one ragged tile of prefix, no split
+    ("greedy64", 1, 1, 0),       # tree keys only
+])
+def test_attention_small_batch_parity(tree, B, nh, L):
+    say("attention (small batch)", tree, B, nh, L)
+    spec = {"dense32": (oracle.dense_paths(3, 2), 3, 2), "chain5": (CHAIN5, 5, 1),
+            "greedy40": (oracle.greedy_paths(configs.acc_exact, 4, 40, 10), 4, 10),
+            "greedy64": (oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10)}[tree]
+    ot, t, q, kt, vt, kc, vc = attn_case("bf16", *spec, B, nh, 128, L, seed=11 * B + L)
+    got = run_attn("bf16", t, q, kt, vt, kc, vc)
+    f = synth.as_f64
+    check_attn("bf16", got, oracle.tree_attention(f(q), f(kt), f(vt), f(kc), f(vc), ot))
+
+
+def test_attention_small_batch_rising_scores():
+    # every query of a head close to one direction v, the cached keys along v
+    # with a weight that rises with the position: scores climb by ~40 log2
+    # units along the prefix, so the running maximum moves with nearly every
+    # tile and every slice's maximum differs; the tree keys are plain noise
+    # and score low
+    paths = oracle.greedy_paths(configs.acc_exact, 4, 63, 10)
+    B, nh, dh, L = 1, 2, 128, 2048
+    ot, t, q, kt, vt, kc, vc = attn_case("bf16", paths, 4, 10, B, nh, dh, L, seed=23)
+    f = synth.as_f64
+    g = rng(29)
+    v = g.standard_normal((nh, dh))
+    v /= np.linalg.norm(v, axis=-1, keepdims=True)
+    q2 = v[None, None] * np.sqrt(dh) + 0.3 * g.standard_normal(f(q).shape)
+    ramp = (np.arange(L) / L * 28.0)[None, None, :, None]
+    kc2 = ramp * v[None, :, None, :] + 0.3 * g.standard_normal(f(kc).shape)
+    q2, kc2 = store(q2.astype(np.float32), "bf16"), store(kc2.astype(np.float32), "bf16")
+    s = np.einsum("bthd,bhld->bthl", f(q2), f(kc2)) / np.sqrt(dh) * np.log2(np.e)
+    assert (s.max(-1) - s.min(-1)).min() > 30      # the climb the case is for
+    got = run_attn("bf16", t, q2, kt, vt, kc2, vc)
+    check_attn("bf16", got, oracle.tree_attention(f(q2), f(kt), f(vt), f(kc2), f(vc), ot))
+
+
 # The wide kernel (bf16, dh = 128, 65..384 tree tokens): one block per
 # (b, head), 4 / 8 / 12 waves of 32 nodes; prefix slices and the merge when
 # the (b, head) pairs are fewer than the CUs.
@@ -459,14 +503,14 @@ def accept_case(paths, K, k, B, V, seed, cfg_id=77):
     return ot, t, tok, logits
 
 
-def run_accept(t, logits, tok, eps, delta, tau):
+def run_accept(t, logits, tok, eps, delta, tau, ws=None):
     B, T, V = logits.shape
     o = {n: torch.full((B,), -9, dtype=torch.int32, device="cuda") for n in ("accept_len", "best", "next_tok")}
     acc = torch.full((B, t.depth_max + 1), -9, dtype=torch.int32, device="cuda")
     cp = torch.empty((B, T), dtype=torch.float32, device="cuda")
     th = torch.empty((B, T), dtype=torch.float32, device="cuda")
     mb.typical_accept(t, dev(logits), dev(tok.astype(np.int32)), eps, delta, tau, o["accept_len"], o["best"],
-                      o["next_tok"], acc, cp, th)
+                      o["next_tok"], acc, cp, th, ws=ws)
     res = {n: host(v) for n, v in o.items()}
     res.update(accepted=host(acc), cand_p=host(cp), row_thr=host(th))
     return res
