@@ -181,6 +181,72 @@ def time_steps(s, n, warmup, copies=1):
     return us, stage
 
 
+def composed_step(s, steps, warmup, copies, seed):
+    """The verify tree-step with its verification logits computed instead of
+    planted: heads on the B sequences' hidden states, top-k and tree tokens,
+    tree attention, then the LM head (a Medusa head with W1 = 0, seeded random
+    weights) over the attention output of all M = B*T nodes, then typical
+    acceptance on those logits.  The attention output stands in for the last
+    hidden state of the verify forward (one attention, no backbone layers), so
+    the accepted lengths mean nothing here; the time of every stage does."""
+    import torch
+    from speculative_decoding_05_amd import binding as mb
+    from speculative_decoding_05_amd import step as st
+    cfg, tree = s.cfg, s.tree
+    B, T, V, H = cfg.B, tree.T, cfg.V, cfg.H
+    vp = st.VerifyPass(s, seed=seed)
+    vl = vp.vlogits.view(B, T, V)
+
+    def accept_lm(i=0):
+        mb.typical_accept(tree, vl, s.tree_tok, cfg.eps, cfg.delta, cfg.temperature, s.accept_len, s.best,
+                          s.next_tok, s.accepted, None, None, s.ws_acc)
+
+    def lm_head(i=0):
+        vp.lm_head()
+
+    names = ["head_resblock", "head_vocab", "topk_tokens", "attention", "lm_head", "accept"]
+    fns = [s.heads, s.heads_vocab, s.topk_and_tokens, s.attention, lm_head, accept_lm]
+
+    def one(i):
+        for fn in fns:
+            fn(i % copies)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        one(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    reps = min(steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    for i in range(reps):
+        evs[i][0].record()
+        for j, fn in enumerate(fns):
+            fn(i % copies)
+            evs[i][j + 1].record()
+    torch.cuda.synchronize()
+    stage = {nm: 1e3 * sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(reps)) / reps
+             for j, nm in enumerate(names)}
+    e = elem(cfg)
+    M = B * T
+    sb, sf = stage_bytes(cfg, tree), stage_flops(cfg, tree)
+    sb["lm_head"] = V * H * e + M * H * e + M * V * 4
+    sf["lm_head"] = 2 * M * H * V
+    roof = {n: max(sb[n] / HBM_PEAK, sf.get(n, 0) / BF16_PEAK) * 1e6 for n in names}
+    out = {"us_per_step": us, "tree_steps_per_s": 1e6 / us, "seq_steps_per_s": B * 1e6 / us, "steps": steps,
+           "lm_head_rows": M, "stage_us": stage, "stage_roofline_us": roof,
+           "step_roofline_us": sum(roof.values()), "roofline_frac_step": sum(roof.values()) / us,
+           "lm_head_bound": "mfma" if sf["lm_head"] / BF16_PEAK > sb["lm_head"] / HBM_PEAK else "hbm",
+           "note": "verification logits from an LM head over the tree-attention output (random weights)"}
+    del vp, vl
+    torch.cuda.empty_cache()
+    return out
+
+
 def tree_sweep(cfg, args):
     """Step time against tree size at the workload's shapes: greedy sparse
     trees of 16..256 nodes and dense trees of about 256 and 340 candidates
@@ -444,6 +510,8 @@ def other_workload(name, steps, warmup):
            "config": {"batch": cfg.B, "hidden": cfg.H, "attn_heads": cfg.nh, "kv_len": cfg.L,
                       "medusa_heads": cfg.K, "tree_nodes": tree.T, "topk": cfg.k},
            "data": "synthetic, drawn on the device (torch generator); planted verification logits"}
+    if name == "roofline_b16":
+        out["verify_step"] = composed_step(s, steps, warmup, copies, seed=cfg.cfg_id)
     del s
     torch.cuda.empty_cache()
     return out
@@ -560,6 +628,8 @@ def main():
     ap.add_argument("--sweep", choices=["trees", "accept"], default=None,
                     help="instead of the headline line: step time per tree size, or acceptance curves")
     ap.add_argument("--graph", type=int, default=1, help="also time the step captured in HIP graphs (0: skip)")
+    ap.add_argument("--composed", type=int, default=100,
+                    help="steps of the verify step with LM-head verification logits (0: skip)")
     ap.add_argument("--verify-reps", type=int, default=10,
                     help="repetitions of each verify-pass contraction (0: skip)")
     ap.add_argument("--event-every", type=int, default=8,
@@ -714,6 +784,9 @@ def main():
     if cfg.dtype == "bf16" and args.verify_reps > 0:
         print("[bench] verify-pass contractions (M = B*T rows)", file=sys.stderr, flush=True)
         res["verify_pass"] = verify_pass(s, args.verify_reps)
+    if cfg.dtype == "bf16" and args.composed > 0:
+        print("[bench] verify step with computed verification logits", file=sys.stderr, flush=True)
+        res["verify_step"] = composed_step(s, args.composed, 10, copies, seed=cfg.cfg_id)
     print(f"[bench] {ms_step * 1e3:.1f} us/step; stages {json.dumps({k: round(v, 1) for k, v in stage_us.items()})}",
           file=sys.stderr, flush=True)
     if args.cpu_seconds > 0:
