@@ -573,9 +573,11 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
 // (global_load_lds_dwordx4: lane i's 16 bytes land at the wave's base + 16 i)
 // in three stages, the loads of tile t+2 issued while tile t is worked on, one
 // barrier per tile.  The 16-byte chunks of each 256-byte row are XOR-swizzled
-// (K: chunk ^ (row & 15), V: chunk ^ 2 (row & 3)) so that the 16 rows of a
-// b128 K read and the 4 rows x 32 bytes of a 16-lane transpose read hit
-// distinct banks; the loads apply the swizzle on the global side (lane i of a
+// (K: chunk ^ (row & 15), V: chunk ^ 4 (row & 3)) so that the 16 rows of a
+// b128 K read hit distinct banks, and so do the two 16-lane groups of a
+// half-wave transpose read (4 rows x 32 bytes each, the same 4 rows, their
+// 32-byte column blocks 64 bytes apart); the loads apply the swizzle on the
+// global side (lane i of a
 // load fills physical chunk i % 16 and fetches the logical chunk that maps
 // there), and a fragment's address is the lane's base XOR the step's offset.
 // The tree mask rows of the block's nodes are copied to LDS once.  The
@@ -702,7 +704,7 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
     const long stride = is_tree ? (long)nh * DH : (long)DH;
     const uint16_t *kb = is_tree ? kt_b : kc_bh;
     const uint16_t *vb = is_tree ? vt_b : vc_bh;
-    const int cv = (lane & 15) ^ ((lane >> 4) << 1);  // row & 3 == lane / 16
+    const int cv = (lane & 15) ^ ((lane >> 4) << 2);  // row & 3 == lane / 16
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
       const int ins = IPW * wave + j;
@@ -724,11 +726,13 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
   // logical chunk 2k + hh, physical (2k + hh) ^ (lq & 15) = base ^ 2k (the
   // step only flips bits 5-7 of the byte address).  V^T read by 16-lane group
   // g: rows 32 st + 16 ks + 4 (g >> 1) + (li >> 2) (+8), logical chunk
-  // 4 d + 2 (g & 1) + (li & 3) / 2, physical that ^ 2 (li >> 2) = base ^ 4d.
+  // 4 d + 2 (g & 1) + (li & 3) / 2, physical that ^ 4 (li >> 2) = base ^ 4d
+  // (over the 32 lanes of groups 2h, 2h+1 the physical chunks are 0..15 once
+  // each: the half-wave read covers the 64 banks exactly).
   const int g = lane >> 4, li = lane & 15;
   const int kaddr = lq * 256 + ((hh ^ (lq & 1)) | (((lq & 15) >> 1) << 1)) * 16;
   const int vaddr = 16384 + (4 * (g >> 1) + (li >> 2)) * 256 +
-                    ((2 * (g & 1) + ((li & 3) >> 1)) ^ ((li >> 2) << 1)) * 16 + (li & 1) * 8;
+                    ((2 * (g & 1) + ((li & 3) >> 1)) ^ ((li >> 2) << 2)) * 16 + (li & 1) * 8;
 
   auto consume = [&](int tile, const u32x4_t *stg) __attribute__((always_inline)) {
     if (!wave_live) return;
