@@ -752,13 +752,14 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
 #pragma unroll
       for (int k = 0; k < KS; ++k) s = mfma32(*reinterpret_cast<const u32x4_t *>(kp + (kaddr ^ (k << 5))), qreg[k], s);
       if (masked) {
-        const uint64_t mw = is_tree ? (qvalid ? wide_mask[tq * W + tt] : 0ull) : ~0ull;
+        // visible keys of the tile as one word (a tree node's mask row has no
+        // bit at or past T; a ragged prefix tile keeps its first kend keys),
+        // then this lane's 16: bit 8 j + i is key 32 st + 8 j + 4 hh + i
+        const uint64_t mw = is_tree ? (qvalid ? wide_mask[tq * W + tt] : 0ull)
+                                    : (kend >= kKT ? ~0ull : (1ull << kend) - 1ull);
+        const uint32_t mb = (static_cast<uint32_t>(mw >> (32 * st)) >> (4 * hh)) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = st * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const bool ok = key < kend && ((mw >> key) & 1ull);
-          s[e] = ok ? s[e] : -INFINITY;
-        }
+        for (int e = 0; e < 16; ++e) s[e] = ((mb >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[e] : -INFINITY;
       }
       float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
