@@ -30,6 +30,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
 BF16_PEAK = 2.5e15         # dense bf16 MFMA, flop/s
+FP32_PEAK = 157.3e12       # fp32 vector (the fp32 path's contractions run on VALU), flop/s
+
+
+def flop_peak(cfg):
+    return BF16_PEAK if cfg.dtype == "bf16" else FP32_PEAK
 METRIC = "Medusa verify tree-steps/sec at 1 GPU (64-node tree, 7B shape); % HBM roofline"
 
 
@@ -473,11 +478,11 @@ def graph_variant(s, copies, steps, warmup):
     return {"us_per_step": us, "steps_per_s": 1e6 / us, "replays_match_eager": bool(match)}
 
 
-OTHER_WORKLOADS = ["roofline_b16", "vicuna13b_b8", "dense341_b32"]
+OTHER_WORKLOADS = ["tiny_f32", "roofline_b16", "vicuna13b_b8", "dense341_b32"]
 
 
 def other_workload(name, steps, warmup):
-    """Whole eager steps of another bf16 workload: inputs drawn on the device
+    """Whole eager steps of another workload: inputs drawn on the device
     (same shapes and distributions as the headline's host-drawn ones),
     verification logits planted at the step's own candidates, per-step inputs
     rotated past the last-level cache.  No verify pass, no oracle."""
@@ -502,7 +507,7 @@ def other_workload(name, steps, warmup):
     us, stage = time_steps(s, steps, warmup, copies)
     sb, sf = stage_bytes(cfg, tree), stage_flops(cfg, tree)
     names = list(stage)
-    roof_s = sum(max(sb[n] / HBM_PEAK, sf.get(n, 0) / BF16_PEAK) for n in names)
+    roof_s = sum(max(sb[n] / HBM_PEAK, sf.get(n, 0) / flop_peak(cfg)) for n in names)
     out = {"tree_steps_per_s": 1e6 / us, "seq_steps_per_s": cfg.B * 1e6 / us, "us_per_step": us,
            "steps": steps, "input_copies": copies, "step_roofline_us": roof_s * 1e6,
            "hbm_roofline_frac_step": roof_s / (us * 1e-6), "stage_us": stage,
@@ -731,7 +736,7 @@ def main():
 
     sb = stage_bytes(cfg, tree)
     sf = stage_flops(cfg, tree)
-    roof_s = sum(max(sb[n] / HBM_PEAK, sf.get(n, 0) / BF16_PEAK) for n in names)
+    roof_s = sum(max(sb[n] / HBM_PEAK, sf.get(n, 0) / flop_peak(cfg)) for n in names)
     vocab_bytes = sb["head_vocab"]
     achieved = vocab_bytes / (vocab_ms * 1e-3)
     res = {

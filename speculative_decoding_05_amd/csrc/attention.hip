@@ -468,10 +468,31 @@ __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T
   *reinterpret_cast<uint2 *>(out + (((size_t)b * T + t) * nh + h) * DH + c) = w;
 }
 
-// fp32 path: block = (b, h, 32 queries); keys = lanes; K/V tiles in LDS.
+// fp32 path: block = (b, h, 32 queries); keys = lanes.  Per 64-key tile each
+// lane holds its own key's K row in registers and scores the wave's 8
+// queries against it (Q rows read from LDS as broadcast float4s); the 8 rows
+// of probabilities go to a per-wave LDS block laid out key-major, so the PV
+// sum reads each V value once for all 8 queries and their 8 probabilities as
+// two broadcast float4s.  Row statistics by DPP row steps and readlane.
 constexpr int kF32Q = 32;
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dppf<kDppXor1>(v));
+  v = fmaxf(v, dppf<kDppXor2>(v));
+  v = fmaxf(v, dppf<kDppHalfMirror>(v));
+  v = fmaxf(v, dppf<kDppMirror>(v));
+  return fmaxf(fmaxf(readlanef(v, 0), readlanef(v, 16)), fmaxf(readlanef(v, 32), readlanef(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dppf<kDppXor1>(v);
+  v += dppf<kDppXor2>(v);
+  v += dppf<kDppHalfMirror>(v);
+  v += dppf<kDppMirror>(v);
+  return (readlanef(v, 0) + readlanef(v, 16)) + (readlanef(v, 32) + readlanef(v, 48));
+}
+
 template <int DH>
-__global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W, int L, int Lstride,
+__global__ __launch_bounds__(256, 1) void tree_attn_f32(int B, int nh, int T, int W, int L, int Lstride,
                                                      const int32_t *__restrict__ seq_len, float scale,
                                                      int qgroups, const float *__restrict__ q,
                                                      const float *__restrict__ kt,
@@ -481,9 +502,10 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
                                                      const uint64_t *__restrict__ mask,
                                                      float *__restrict__ out) {
   constexpr int DPL = DH / 64;  // output dims per lane
-  __shared__ float ks[kKT][DH + 1];
-  __shared__ float vs[kKT][DH];
-  __shared__ float qs[kF32Q][DH];
+  constexpr int D4 = DH / 4;
+  __shared__ __attribute__((aligned(16))) float vs[kKT][DH];
+  __shared__ __attribute__((aligned(16))) float qs[kF32Q][DH];
+  __shared__ __attribute__((aligned(16))) float pw[4][kKT][8];  // per wave: key-major probabilities of its 8 queries
   const int qg = blockIdx.x % qgroups;
   const int h = (blockIdx.x / qgroups) % nh;
   const int b = blockIdx.x / (qgroups * nh);
@@ -507,47 +529,74 @@ __global__ __launch_bounds__(256) void tree_attn_f32(int B, int nh, int T, int W
     const bool is_tree = tile >= ncache;
     const int r0 = is_tree ? (tile - ncache) * kKT : tile * kKT;
     const int rend = is_tree ? T : Lb;
-    __syncthreads();
-    for (int e = threadIdx.x; e < kKT * DH; e += 256) {
-      const int r = e / DH, d = e % DH, row = r0 + r;
-      float kv = 0.f, vv = 0.f;
-      if (row < rend) {
-        const size_t off = is_tree ? (((size_t)b * T + row) * nh + h) * DH + d
-                                   : (((size_t)b * nh + h) * Lstride + row) * DH + d;
-        kv = is_tree ? kt[off] : kc[off];
-        vv = is_tree ? vt[off] : vc[off];
-      }
-      ks[r][d] = kv;
-      vs[r][d] = vv;
-    }
-    __syncthreads();
     const int key = r0 + lane;
+    const int krow = min(key, rend - 1);  // past the end: a valid row, masked below
+    // this lane's K row, and its share of the V tile: all loads issued before any store
+    const float *kp = is_tree ? kt + (((size_t)b * T + krow) * nh + h) * DH
+                              : kc + (((size_t)b * nh + h) * Lstride + krow) * DH;
+    float4 kr[D4];
+#pragma unroll
+    for (int i = 0; i < D4; ++i) kr[i] = *reinterpret_cast<const float4 *>(kp + 4 * i);
+    constexpr int kPer = kKT * DH / 256;
+    float vv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int r = e / DH, d = e % DH, row = r0 + r;
+      vv[i] = 0.f;
+      if (row < rend) {
+        vv[i] = is_tree ? vt[(((size_t)b * T + row) * nh + h) * DH + d]
+                        : vc[(((size_t)b * nh + h) * Lstride + row) * DH + d];
+      }
+    }
+    // the mask words of this wave's 8 queries for a tree tile, loaded together
+    uint64_t mw[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int qi = wave * 8 + u, t = qg * kF32Q + qi;
+      const int t = qg * kF32Q + wave * 8 + u;
+      mw[u] = is_tree && t < T ? mask[(size_t)t * W + (tile - ncache)] : 0ull;
+    }
+    __syncthreads();  // the previous tile's readers are done
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      vs[e / DH][e % DH] = vv[i];
+    }
+    __syncthreads();
+    // scores of the wave's 8 queries against this lane's key; online softmax
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int qi = wave * 8 + u;
       float s = 0.f;
-#pragma unroll 8
-      for (int d = 0; d < DH; ++d) s += qs[qi][d] * ks[lane][d];
+#pragma unroll
+      for (int i = 0; i < D4; ++i) {
+        const float4 qv = *reinterpret_cast<const float4 *>(&qs[qi][4 * i]);
+        s += qv.x * kr[i].x + qv.y * kr[i].y + qv.z * kr[i].z + qv.w * kr[i].w;
+      }
       bool ok = key < rend;
-      if (is_tree) ok = ok && t < T && ((mask[(size_t)t * W + (tile - ncache)] >> lane) & 1ull);
-      float x = ok ? s * scale : -INFINITY;
-      float mx = x;
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float m_new = fmaxf(m[u], mx);
+      if (is_tree) ok = ok && ((mw[u] >> lane) & 1ull);
+      const float x = ok ? s * scale : -INFINITY;
+      const float m_new = fmaxf(m[u], wave_max_f32(x));
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = expf(m[u] - m_use);
       const float p = expf(x - m_use);
-      float ps = p;
-      for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-      l[u] = l[u] * alpha + ps;
+      l[u] = l[u] * alpha + wave_sum_f32(p);
       m[u] = m_new;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) o[u][j] *= alpha;
+      pw[wave][lane][u] = p;  // the same wave reads it back below: LDS keeps the order
+    }
+    // O += P V: each V value once, the 8 probabilities of its key as two float4s
 #pragma unroll 4
-      for (int jk = 0; jk < kKT; ++jk) {
-        const float pj = __shfl(p, jk);
+    for (int jk = 0; jk < kKT; ++jk) {
+      const float4 pa = *reinterpret_cast<const float4 *>(&pw[wave][jk][0]);
+      const float4 pb = *reinterpret_cast<const float4 *>(&pw[wave][jk][4]);
+      const float pu[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
-        for (int j = 0; j < DPL; ++j) o[u][j] += pj * vs[jk][lane + 64 * j];
+      for (int j = 0; j < DPL; ++j) {
+        const float v = vs[jk][lane + 64 * j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u][j] += pu[u] * v;
       }
     }
   }
