@@ -906,10 +906,19 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
   }
 }
 
-// The wide kernel serves dh = 128 trees of 65..384 tokens.  (Measured on
-// MI355X at batch 1 with the 64-node tree: two waves per block over 8 prefix
-// slices are slower than the 64-query kernel, 14.6 + 4.4 against 13.9 + 4.4 us.)
-inline bool use_wide(medusa_dtype dt, int dh, int T) { return dt == MEDUSA_BF16 && dh == 128 && T > kQB && T <= 384; }
+// The wide kernel serves dh = 128 trees of 129..384 tokens, and of 65..128
+// tokens while the (b, head) pairs are at most one per CU; past that the
+// 128-query kernel, two blocks per CU, is faster for the small trees
+// (measured on MI355X, 128 nodes, KV 1024: wide 21.7 / 34.8 / 43.6 us at
+// 32 / 128 / 256 pairs against 26.8 / 47.4 / 51.0, but 92.4 against 69.5 at
+// 512 pairs, and 254.6 against 173.7 us at the 13B shape's 320 pairs with
+// KV 4096).  (At batch 1 with the 64-node tree, two waves per block over 8
+// prefix slices are slower than the 64-query kernel, 14.6 + 4.4 against
+// 13.9 + 4.4 us.)
+inline bool use_wide(medusa_dtype dt, int dh, int T, int B, int nh) {
+  if (dt != MEDUSA_BF16 || dh != 128 || T <= kQB || T > 384) return false;
+  return T > 2 * kQB || (long)B * nh <= device_compute_units();
+}
 inline int wide_waves(int T) { return T <= 128 ? 4 : T <= 256 ? 8 : 12; }
 
 // One block per (b, head) already fills the chip from one block per CU; with
@@ -1021,7 +1030,7 @@ medusa_status launch_f32(hipStream_t st, const medusa_tree *t, int B, int nh, Pr
 extern "C" size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t, int B, int nh,
                                            int dh, int L) {
   if (!t || B < 1 || nh < 1 || dh < 1 || L < 0 || dt != MEDUSA_BF16) return 0;
-  const Split sp = use_wide(dt, dh, t->T) ? choose_split_wide(B, nh, L) : choose_split(B, nh, t->T, L);
+  const Split sp = use_wide(dt, dh, t->T, B, nh) ? choose_split_wide(B, nh, L) : choose_split(B, nh, t->T, L);
   if (sp.nsplit == 1) return 0;
   return (size_t)sp.nsplit * B * nh * t->T * (dh + 2) * sizeof(float);
 }
@@ -1051,7 +1060,7 @@ medusa_status attention_entry(const char *who, medusa_stream_t stream, medusa_dt
   if (need > 0 && !aligned16(ws)) return fail(MEDUSA_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
   const float sc = scale == 0.f ? 1.0f / sqrtf((float)dh) : scale;
   hipStream_t st = as_stream(stream);
-  if (use_wide(dt, dh, t->T)) {
+  if (use_wide(dt, dh, t->T, B, nh)) {
     const Split sp = choose_split_wide(B, nh, L);
     const int nw = wide_waves(t->T);
     return nw == 4 ? launch_wide<4>(st, t, B, nh, pf, sp, sc, q, k_tree, v_tree, k_cache, v_cache, out, ws)

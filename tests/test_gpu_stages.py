@@ -354,6 +354,9 @@ CHAIN5 = [[0] * d for d in range(1, 6)]
     # with two prefix slices (the second ragged: 280 keys)
     ("bf16", "greedy64", 2, 150, 128, 600),
     ("bf16", "dense32", 3, 100, 64, 600),
+    # 65..128 tree tokens with more (b, head) pairs than CUs: the 128-query tiles
+    ("bf16", "greedy128", 2, 150, 128, 300),
+    ("bf16", "dense34", 3, 100, 128, 130),
     ("f32", "dense22", 1, 4, 64, 128),         # the tiny fp32 configuration
     ("f32", "dense32", 2, 2, 128, 77),
 ])
@@ -361,7 +364,9 @@ def test_attention_parity(dtype, tree, B, nh, dh, L):
     say("attention", dtype, tree, B, nh, dh, L)
     spec = {"dense32": (oracle.dense_paths(3, 2), 3, 2), "chain5": (CHAIN5, 5, 1), "root": ([], 1, 1),
             "dense44": (oracle.dense_paths(4, 4), 4, 4), "dense22": (oracle.dense_paths(2, 2), 2, 2),
-            "greedy64": (oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10)}[tree]
+            "dense34": (oracle.dense_paths(3, 4), 3, 4),
+            "greedy64": (oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10),
+            "greedy128": (oracle.greedy_paths(configs.acc_exact, 4, 127, 10), 4, 10)}[tree]
     ot, t, q, kt, vt, kc, vc = attn_case(dtype, *spec, B, nh, dh, L, seed=B * 100 + L)
     got = run_attn(dtype, t, q, kt, vt, kc, vc)
     f = synth.as_f64
