@@ -693,6 +693,9 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
   constexpr int DT = DH / 32;          // 32-wide output tiles
   constexpr int LW = NW < 8 ? NW : 8;  // waves that issue the tile loads
   constexpr int IPW = 16 / LW;         // 1 KiB K loads (and as many V loads) per loader wave per tile
+  // the two 32-key halves of a tile unrolled where registers allow (two waves
+  // per SIMD or fewer: 256 registers; with three, 168 do not hold both)
+  constexpr int kHalves = NW <= 8 ? 2 : 1;
   const int split = blockIdx.x % nsplit;
   const int bh = blockIdx.x / nsplit;
   const int h = bh % nh, b = bh / nh;
@@ -791,8 +794,8 @@ __global__ __launch_bounds__(64 * NW, 1) void tree_attn_wide_bf16(
     const int kend = is_tree ? T - tt * kKT : c1 - (c0 + tile * kKT);
     const bool masked = is_tree || kend < kKT;
     const char *base = reinterpret_cast<const char *>(stg);
-#pragma unroll 1
-    for (int st = 0; st < 2; ++st) {  // 32-key halves of the tile (not unrolled: register budget)
+#pragma unroll kHalves
+    for (int st = 0; st < 2; ++st) {  // 32-key halves of the tile
       // S^T: lane holds S[key 32 st + 8 j + 4 hh + i][tq] in s[4 j + i]
       f32x16_t s;
 #pragma unroll
