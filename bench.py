@@ -481,11 +481,12 @@ def graph_variant(s, copies, steps, warmup):
 OTHER_WORKLOADS = ["tiny_f32", "roofline_b16", "vicuna13b_b8", "dense341_b32"]
 
 
-def other_workload(name, steps, warmup):
+def other_workload(name, steps, warmup, verify_reps=0):
     """Whole eager steps of another workload: inputs drawn on the device
     (same shapes and distributions as the headline's host-drawn ones),
     verification logits planted at the step's own candidates, per-step inputs
-    rotated past the last-level cache.  No verify pass, no oracle."""
+    rotated past the last-level cache; for bf16 workloads also the verify-pass
+    contractions (`verify_reps` timed calls each).  No oracle."""
     import torch
     from speculative_decoding_05_amd import configs
     from speculative_decoding_05_amd import step as st
@@ -517,6 +518,8 @@ def other_workload(name, steps, warmup):
            "data": "synthetic, drawn on the device (torch generator); planted verification logits"}
     if name == "roofline_b16":
         out["verify_step"] = composed_step(s, steps, warmup, copies, seed=cfg.cfg_id)
+    if cfg.dtype == "bf16" and verify_reps > 0:
+        out["verify_pass"] = verify_pass(s, verify_reps)
     del s
     torch.cuda.empty_cache()
     return out
@@ -807,7 +810,7 @@ def main():
         for name in OTHER_WORKLOADS:
             print(f"[bench] other workload {name}", file=sys.stderr, flush=True)
             n = 40 if name == "dense341_b32" else 100
-            res["other_workloads"][name] = other_workload(name, n, 10)
+            res["other_workloads"][name] = other_workload(name, n, 10, args.verify_reps)
     print(json.dumps(res), flush=True)
 
 
