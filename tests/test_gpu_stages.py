@@ -418,7 +418,8 @@ def test_attention_small_batch_rising_scores():
     check_attn("bf16", got, oracle.tree_attention(f(q2), f(kt), f(vt), f(kc2), f(vc), ot))
 
 
-# The wide kernel (bf16, dh = 128, 65..384 tree tokens): one block per
+# The wide kernel (bf16, dh = 128, 129..384 tree tokens, or 65..128 with at
+# most one (b, head) pair per CU): one block per
 # (b, head), 4 / 8 / 12 waves of 32 nodes; prefix slices and the merge when
 # the (b, head) pairs are fewer than the CUs.
 @pytest.mark.parametrize("tree,B,nh,L", [
