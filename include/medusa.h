@@ -284,7 +284,10 @@ medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const medusa_tree 
  *  k_cache, v_cache   [B][nh][L][dh]  device, dt  (the prefix cache; L may be 0)
  *  out                [B][T][nh][dh]  device, dt  (output)
  *  scale: 0 means 1/sqrt(dh).  Limits: dh in {64, 128}.
- *  ws: tree_attention_workspace bytes (split-prefix partial results). */
+ *  ws: tree_attention_workspace bytes (split-prefix partial results).  The
+ *  size, like the kernel chosen, depends on the current device's compute
+ *  units: query it with the device current that the call will run on (a
+ *  smaller workspace is refused with MEDUSA_ERR_WORKSPACE, never overrun). */
 size_t tree_attention_workspace(medusa_dtype dt, const medusa_tree *t, int B, int nh, int dh,
                                 int L);
 medusa_status tree_attention(medusa_stream_t stream, medusa_dtype dt, const medusa_tree *t,
