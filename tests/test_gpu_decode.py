@@ -51,24 +51,31 @@ def test_ragged_attention_three_blocks_per_cu():
             assert rel_err(got[b, :, h], ref[b, :, h]) <= TOL["bf16"], (b, h)
 
 
-@pytest.mark.parametrize("dtype,paths,dh,L_cap,lens", [
-    ("bf16", "greedy64", 128, 700, [0, 64, 300, 651, 700]),   # several prefix slices
-    ("bf16", "dense44", 128, 1100, [0, 333, 1100]),           # 341 nodes: the wide kernel, 4 slices
-    ("bf16", "dense22", 64, 90, [5, 0, 90]),
-    ("f32", "dense22", 64, 140, [0, 77, 129]),
+@pytest.mark.parametrize("dtype,paths,dh,L_cap,lens,nh", [
+    ("bf16", "greedy64", 128, 700, [0, 64, 300, 651, 700], 2),   # several prefix slices
+    ("bf16", "dense44", 128, 1100, [0, 333, 1100], 2),           # 341 nodes: the wide kernel, 4 slices
+    ("bf16", "greedy256", 128, 500, [0, 257, 500], 2),           # 256 nodes: the 8-wave wide build
+    # 128 nodes over 300 (b, head) pairs, more than the CUs: the 128-query kernel
+    ("bf16", "greedy128", 128, 400, [0, 130, 400], 100),
+    ("bf16", "dense22", 64, 90, [5, 0, 90], 2),
+    ("f32", "dense22", 64, 140, [0, 77, 129], 2),
 ])
-def test_ragged_attention_parity(dtype, paths, dh, L_cap, lens):
+def test_ragged_attention_parity(dtype, paths, dh, L_cap, lens, nh):
     if paths == "greedy64":
         p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10
+    elif paths == "greedy128":
+        p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 127, 10), 4, 10
+    elif paths == "greedy256":
+        p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 255, 10), 4, 10
     elif paths == "dense44":
         p, K, k = oracle.dense_paths(4, 4), 4, 4
     else:
         p, K, k = oracle.dense_paths(2, 2), 2, 2
     ot = oracle.build_tree(p, K, k)
     t = mb.Tree(p, K, k).upload()
-    B, nh, T = len(lens), 2, ot["T"]
+    B, T = len(lens), ot["T"]
     L_max = max(lens)
-    say("ragged attention", dtype, paths, dh, L_cap, lens)
+    say("ragged attention", dtype, paths, dh, L_cap, lens, nh)
     g = rng(len(lens) * 100 + dh)
     mk = lambda shape: store(g.standard_normal(shape).astype(np.float32), dtype)
     q, kt, vt = mk((B, T, nh, dh)), mk((B, T, nh, dh)), mk((B, T, nh, dh))
