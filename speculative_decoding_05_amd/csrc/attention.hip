@@ -468,12 +468,19 @@ __global__ __launch_bounds__(256) void tree_attn_merge_bf16(int B, int nh, int T
   *reinterpret_cast<uint2 *>(out + (((size_t)b * T + t) * nh + h) * DH + c) = w;
 }
 
-// fp32 path: block = (b, h, 32 queries); keys = lanes.  Per 64-key tile each
-// lane holds its own key's K row in registers and scores the wave's 8
+// fp32 path: block = (b, h, 32 queries); keys = lanes.  The block's 4 waves
+// are QW query waves (8 queries each, as many as the group's queries need) x
+// KW key splits (KW = 4 / QW): wave (qw, kw) takes tiles kw, kw + KW, ... of
+// the keys for its 8 queries, so a small tree (8 queries or fewer) spreads its
+// tiles over all four waves.  Each wave stages its own V tile in its own LDS
+// region (global_load_lds_dwordx4: the rows land in order, no staging
+// registers) and needs no block barrier inside the loop.  Per 64-key tile
+// each lane holds its own key's K row in registers and scores the wave's 8
 // queries against it (Q rows read from LDS as broadcast float4s); the 8 rows
 // of probabilities go to a per-wave LDS block laid out key-major, so the PV
 // sum reads each V value once for all 8 queries and their 8 probabilities as
-// two broadcast float4s.  Row statistics by DPP row steps and readlane.
+// two broadcast float4s.  Row statistics by DPP row steps and readlane.  At
+// the end the KW partial (max, sum, O) of each query are merged through LDS.
 constexpr int kF32Q = 32;
 
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -491,6 +498,18 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (readlanef(v, 0) + readlanef(v, 16)) + (readlanef(v, 32) + readlanef(v, 48));
 }
 
+// LDS of the fp32 kernel, in floats: per-wave V tiles, the Q rows of the
+// group, per-wave probability blocks; the merge area reuses the V tiles
+template <int DH>
+struct F32Lds {
+  static constexpr int kV = 0, kVWave = kKT * DH;
+  static constexpr int kQ = 4 * kVWave;
+  static constexpr int kP = kQ + kF32Q * DH;
+  static constexpr int kTotal = kP + 4 * kKT * 8;
+  static_assert(4 * 8 * (DH + 2) <= 4 * kVWave, "merge area");
+  static_assert(kTotal * 4 <= 160 * 1024, "LDS");
+};
+
 template <int DH>
 __global__ __launch_bounds__(256, 1) void tree_attn_f32(int B, int nh, int T, int W, int L, int Lstride,
                                                      const int32_t *__restrict__ seq_len, float scale,
@@ -501,19 +520,27 @@ __global__ __launch_bounds__(256, 1) void tree_attn_f32(int B, int nh, int T, in
                                                      const float *__restrict__ vc,
                                                      const uint64_t *__restrict__ mask,
                                                      float *__restrict__ out) {
-  constexpr int DPL = DH / 64;  // output dims per lane
+  using LY = F32Lds<DH>;
+  constexpr int DPL = DH / 64;            // output dims per lane
   constexpr int D4 = DH / 4;
-  __shared__ __attribute__((aligned(16))) float vs[kKT][DH];
-  __shared__ __attribute__((aligned(16))) float qs[kF32Q][DH];
-  __shared__ __attribute__((aligned(16))) float pw[4][kKT][8];  // per wave: key-major probabilities of its 8 queries
+  constexpr int RPI = 64 / (DH / 4);      // V rows per 1 KiB wave load (16 bytes per lane)
+  __shared__ __attribute__((aligned(16))) float lds[LY::kTotal];
   const int qg = blockIdx.x % qgroups;
   const int h = (blockIdx.x / qgroups) % nh;
   const int b = blockIdx.x / (qgroups * nh);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int Tq = min(kF32Q, T - qg * kF32Q);      // queries of this group
+  const int QW = (Tq + 7) / 8, KW = 4 / QW;       // query waves x key splits
+  const int qw = wave % QW, kw = wave / QW;
+  const bool busy = kw < KW;
+  float *qs = lds + LY::kQ;
+  float *vs = lds + LY::kV + wave * LY::kVWave;
+  float *pw = lds + LY::kP + wave * kKT * 8;
   for (int e = threadIdx.x; e < kF32Q * DH; e += 256) {
     const int qi = e / DH, d = e % DH, t = qg * kF32Q + qi;
-    qs[qi][d] = t < T ? q[(((size_t)b * T + t) * nh + h) * DH + d] : 0.f;
+    qs[e] = t < T ? q[(((size_t)b * T + t) * nh + h) * DH + d] : 0.f;
   }
+  __syncthreads();
   float m[8], l[8], o[8][DPL];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
@@ -525,87 +552,110 @@ __global__ __launch_bounds__(256, 1) void tree_attn_f32(int B, int nh, int T, in
   const int Lb = seq_len ? min(max(seq_len[b], 0), L) : L;
   const int ncache = (Lb + kKT - 1) / kKT;
   const int ntiles = ncache + (T + kKT - 1) / kKT;
-  for (int tile = 0; tile < ntiles; ++tile) {
+  const int q0 = qg * kF32Q + qw * 8;   // the wave's first query
+  for (int tile = busy ? kw : ntiles; tile < ntiles; tile += KW) {
     const bool is_tree = tile >= ncache;
     const int r0 = is_tree ? (tile - ncache) * kKT : tile * kKT;
     const int rend = is_tree ? T : Lb;
     const int key = r0 + lane;
-    const int krow = min(key, rend - 1);  // past the end: a valid row, masked below
-    // this lane's K row, and its share of the V tile: all loads issued before any store
+    // the V tile straight into this wave's region (rows past the end: a valid
+    // row, weighted 0), this lane's K row, the mask words of the 8 queries
+    const float *vbase = is_tree ? vt + ((size_t)b * T * nh + h) * DH : vc + ((size_t)b * nh + h) * Lstride * DH;
+    const long vstride = is_tree ? (long)nh * DH : (long)DH;
+#pragma unroll
+    for (int j = 0; j < kKT / RPI; ++j) {
+      const int row = min(r0 + RPI * j + lane / (DH / 4), rend - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1))) *)(vbase + row * vstride + (lane % (DH / 4)) * 4),
+          (void __attribute__((address_space(3))) *)(vs + j * RPI * DH), 16, 0, 0);
+    }
+    const int krow = min(key, rend - 1);
     const float *kp = is_tree ? kt + (((size_t)b * T + krow) * nh + h) * DH
                               : kc + (((size_t)b * nh + h) * Lstride + krow) * DH;
     float4 kr[D4];
 #pragma unroll
     for (int i = 0; i < D4; ++i) kr[i] = *reinterpret_cast<const float4 *>(kp + 4 * i);
-    constexpr int kPer = kKT * DH / 256;
-    float vv[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int r = e / DH, d = e % DH, row = r0 + r;
-      vv[i] = 0.f;
-      if (row < rend) {
-        vv[i] = is_tree ? vt[(((size_t)b * T + row) * nh + h) * DH + d]
-                        : vc[(((size_t)b * nh + h) * Lstride + row) * DH + d];
-      }
-    }
-    // the mask words of this wave's 8 queries for a tree tile, loaded together
     uint64_t mw[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = qg * kF32Q + wave * 8 + u;
-      mw[u] = is_tree && t < T ? mask[(size_t)t * W + (tile - ncache)] : 0ull;
-    }
-    __syncthreads();  // the previous tile's readers are done
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      vs[e / DH][e % DH] = vv[i];
-    }
-    __syncthreads();
+    for (int u = 0; u < 8; ++u) mw[u] = is_tree && q0 + u < T ? mask[(size_t)(q0 + u) * W + (tile - ncache)] : 0ull;
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the V tile is in LDS
     // scores of the wave's 8 queries against this lane's key; online softmax
+    float x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int qi = wave * 8 + u;
-      float s = 0.f;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < D4; ++i) {
-        const float4 qv = *reinterpret_cast<const float4 *>(&qs[qi][4 * i]);
-        s += qv.x * kr[i].x + qv.y * kr[i].y + qv.z * kr[i].z + qv.w * kr[i].w;
+        const float4 qv = *reinterpret_cast<const float4 *>(&qs[(qw * 8 + u) * DH + 4 * i]);
+        s4[i & 3] += qv.x * kr[i].x + qv.y * kr[i].y + qv.z * kr[i].z + qv.w * kr[i].w;
       }
       bool ok = key < rend;
       if (is_tree) ok = ok && ((mw[u] >> lane) & 1ull);
-      const float x = ok ? s * scale : -INFINITY;
-      const float m_new = fmaxf(m[u], wave_max_f32(x));
+      x[u] = ok ? ((s4[0] + s4[1]) + (s4[2] + s4[3])) * scale : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float m_new = fmaxf(m[u], wave_max_f32(x[u]));
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = expf(m[u] - m_use);
-      const float p = expf(x - m_use);
+      const float p = expf(x[u] - m_use);
       l[u] = l[u] * alpha + wave_sum_f32(p);
       m[u] = m_new;
 #pragma unroll
       for (int j = 0; j < DPL; ++j) o[u][j] *= alpha;
-      pw[wave][lane][u] = p;  // the same wave reads it back below: LDS keeps the order
+      pw[lane * 8 + u] = p;  // the same wave reads it back below: LDS keeps the order
     }
     // O += P V: each V value once, the 8 probabilities of its key as two float4s
 #pragma unroll 4
     for (int jk = 0; jk < kKT; ++jk) {
-      const float4 pa = *reinterpret_cast<const float4 *>(&pw[wave][jk][0]);
-      const float4 pb = *reinterpret_cast<const float4 *>(&pw[wave][jk][4]);
+      const float4 pa = *reinterpret_cast<const float4 *>(&pw[jk * 8]);
+      const float4 pb = *reinterpret_cast<const float4 *>(&pw[jk * 8 + 4]);
       const float pu[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
 #pragma unroll
       for (int j = 0; j < DPL; ++j) {
-        const float v = vs[jk][lane + 64 * j];
+        const float v = vs[jk * DH + lane + 64 * j];
 #pragma unroll
         for (int u = 0; u < 8; ++u) o[u][j] += pu[u] * v;
       }
     }
   }
+  // merge the KW partials of each query: waves kw > 0 leave theirs in LDS
+  // (over the V tiles), the kw = 0 wave of each query wave combines
+  __syncthreads();
+  float *mo = lds + LY::kV;
+  if (busy && kw > 0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float *row = mo + (wave * 8 + u) * (DH + 2);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) row[lane + 64 * j] = o[u][j];
+      if (lane == 0) {
+        row[DH] = m[u];
+        row[DH + 1] = l[u];
+      }
+    }
+  }
+  __syncthreads();
+  if (!busy || kw > 0) return;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int t = qg * kF32Q + wave * 8 + u;
+    const int t = q0 + u;
     if (t >= T) continue;
+    float M = m[u];
+    for (int k = 1; k < KW; ++k) M = fmaxf(M, mo[((qw + k * QW) * 8 + u) * (DH + 2) + DH]);
+    const float w0 = expf(m[u] - M);
+    float lt = l[u] * w0, ot[DPL];
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) out[(((size_t)b * T + t) * nh + h) * DH + lane + 64 * j] = o[u][j] / l[u];
+    for (int j = 0; j < DPL; ++j) ot[j] = o[u][j] * w0;
+    for (int k = 1; k < KW; ++k) {
+      const float *row = mo + ((qw + k * QW) * 8 + u) * (DH + 2);
+      const float wk = row[DH] == -INFINITY ? 0.f : expf(row[DH] - M);
+      lt += row[DH + 1] * wk;
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) ot[j] += row[lane + 64 * j] * wk;
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) out[(((size_t)b * T + t) * nh + h) * DH + lane + 64 * j] = ot[j] / lt;
   }
 }
 
