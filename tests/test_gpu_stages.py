@@ -357,14 +357,19 @@ CHAIN5 = [[0] * d for d in range(1, 6)]
     # 65..128 tree tokens with more (b, head) pairs than CUs: the 128-query tiles
     ("bf16", "greedy128", 2, 150, 128, 300),
     ("bf16", "dense34", 3, 100, 128, 130),
-    ("f32", "dense22", 1, 4, 64, 128),         # the tiny fp32 configuration
-    ("f32", "dense32", 2, 2, 128, 77),
+    ("f32", "dense22", 1, 4, 64, 128),         # the tiny fp32 configuration: 4 key splits
+    ("f32", "dense32", 2, 2, 128, 77),         # 15 nodes: 2 query waves x 2 key splits
+    ("f32", "greedy20", 1, 3, 64, 200),        # 21 nodes: 3 query waves, the fourth wave idle
+    # 341 nodes: 11 query groups per head, the last of 21 queries; ragged prefix
+    ("f32", "dense44", 1, 2, 64, 70),
+    ("f32", "dense44", 1, 1, 128, 130),
 ])
 def test_attention_parity(dtype, tree, B, nh, dh, L):
     say("attention", dtype, tree, B, nh, dh, L)
     spec = {"dense32": (oracle.dense_paths(3, 2), 3, 2), "chain5": (CHAIN5, 5, 1), "root": ([], 1, 1),
             "dense44": (oracle.dense_paths(4, 4), 4, 4), "dense22": (oracle.dense_paths(2, 2), 2, 2),
             "dense34": (oracle.dense_paths(3, 4), 3, 4),
+            "greedy20": (oracle.greedy_paths(configs.acc_exact, 4, 20, 10), 4, 10),
             "greedy64": (oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10),
             "greedy128": (oracle.greedy_paths(configs.acc_exact, 4, 127, 10), 4, 10)}[tree]
     ot, t, q, kt, vt, kc, vc = attn_case(dtype, *spec, B, nh, dh, L, seed=B * 100 + L)
