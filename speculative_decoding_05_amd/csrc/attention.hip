@@ -19,6 +19,13 @@
 // registers; full prefix tiles skip masking.  With more than one slice per
 // (b, h) the blocks write unnormalised partials (O, m, l) and a second kernel
 // merges them with log-sum-exp weights.
+//
+// Three kernels, chosen per call: this one (bf16 trees of up to 64 tokens and
+// of more than 384; trees of 65..128 tokens when the (b, head) pairs
+// outnumber the CUs); tree_attn_wide_bf16 further down (bf16, dh = 128,
+// trees of 129..384 tokens, or of 65..128 at up to one (b, head) pair per CU:
+// one block covers the whole tree, so the prefix is read once per (b, head));
+// and tree_attn_f32 (fp32, any tree).
 #include <math.h>
 
 #include "common.h"
