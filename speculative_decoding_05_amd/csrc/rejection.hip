@@ -278,6 +278,163 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_kernel(
     accepted_tok[(size_t)b * (depth_max + 1) + i] = tree_tok[(size_t)b * T + path[i]];
 }
 
+// The same walk with the distributions held on chip, for V <= 1024 * C: p in
+// registers (thread t owns v = t + 1024 j, j < C, the order in which the
+// streaming kernel above sums, so p, q, every normaliser and every keep
+// probability come out bit for bit the same), q in LDS.  A rejection costs
+// one block sum (the residual is updated in place, never recomputed from the
+// rows), and the final draw scans p from LDS.
+template <int C>
+__global__ __launch_bounds__(kThreads) void rejection_accept_regs(
+    int T, int V, int depth_max, const int32_t *__restrict__ parent, const int32_t *__restrict__ depth,
+    const int32_t *__restrict__ dstart, const float *__restrict__ logits, const float *__restrict__ head_logits,
+    int B, const int32_t *__restrict__ tree_tok, float tau, const float *__restrict__ u_node,
+    const float *__restrict__ u_bonus, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
+    int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ keep_prob) {
+  __shared__ BlockScratch scr;
+  __shared__ int cld[MEDUSA_MAX_TREE];
+  __shared__ int path[MEDUSA_MAX_TREE];
+  __shared__ float s_part[kThreads];
+  __shared__ float s_dist[kThreads * C];
+  __shared__ int s_ncld, s_kept, s_tok;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (keep_prob)
+    for (int c = tid; c < T; c += kThreads) keep_prob[(size_t)b * T + c] = __builtin_nanf("");
+  for (int i = tid; i <= depth_max; i += kThreads) accepted_tok[(size_t)b * (depth_max + 1) + i] = -1;
+
+  // this thread's values of p over the vocabulary (0 past V)
+  auto load_dist = [&](float (&d)[C], const float *row) {
+    if (tau == 0.f) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const int v = tid + kThreads * j;
+        if (v < V) {
+          const uint64_t key = argmax_key(row[v], v);
+          best = key > best ? key : best;
+        }
+      }
+      const int amax = (int)(~(uint32_t)block_max_u64(best, scr));
+#pragma unroll
+      for (int j = 0; j < C; ++j) d[j] = tid + kThreads * j == amax ? 1.f : 0.f;
+      return;
+    }
+    const float inv_tau = 1.f / tau;
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {   // the scaled logits first, in place
+      const int v = tid + kThreads * j;
+      d[j] = v < V ? row[v] * inv_tau : -INFINITY;
+      m = fmaxf(m, d[j]);
+    }
+    m = block_max(m, scr);
+    float S = 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      d[j] = tid + kThreads * j < V ? __expf(d[j] - m) : 0.f;
+      S += d[j];
+    }
+    S = block_sum(S, scr);
+#pragma unroll
+    for (int j = 0; j < C; ++j) d[j] = d[j] / S;
+  };
+
+  // q into s_dist (0 past V), by rolled loops: the same values as load_dist
+  auto load_q = [&](const float *row) {
+    if (tau == 0.f) {
+      uint64_t best = 0;
+      for (int v = tid; v < V; v += kThreads) {
+        const uint64_t key = argmax_key(row[v], v);
+        best = key > best ? key : best;
+      }
+      const int amax = (int)(~(uint32_t)block_max_u64(best, scr));
+      for (int v = tid; v < kThreads * C; v += kThreads) s_dist[v] = v == amax ? 1.f : 0.f;
+    } else {
+      const float inv_tau = 1.f / tau;
+      float m = -INFINITY;
+      for (int v = tid; v < V; v += kThreads) m = fmaxf(m, row[v] * inv_tau);
+      m = block_max(m, scr);
+      float S = 0.f;
+      for (int v = tid; v < V; v += kThreads) S += __expf(row[v] * inv_tau - m);
+      S = block_sum(S, scr);
+      for (int v = tid; v < kThreads * C; v += kThreads) s_dist[v] = v < V ? __expf(row[v] * inv_tau - m) / S : 0.f;
+    }
+    __syncthreads();
+  };
+
+  float pv[C];
+  int u = 0, plen = 1;
+  if (tid == 0) path[0] = 0;
+  while (true) {
+    load_dist(pv, logits + ((size_t)b * T + u) * V);
+    const int d = depth[u];
+    if (tid == 0) {
+      int n = 0;
+      if (d < depth_max)
+        for (int c = dstart[d + 1]; c < dstart[d + 2]; ++c)
+          if (parent[c] == u) cld[n++] = c;
+      s_ncld = n;
+    }
+    __syncthreads();
+    const int ncld = s_ncld;
+    if (ncld == 0) break;                                   // leaf: draw from p
+    load_q(head_logits + ((size_t)d * B + b) * V);
+    int kept = -1;
+    for (int i = 0; i < ncld; ++i) {
+      const int c = cld[i];
+      const int x = tree_tok[(size_t)b * T + c];
+      const bool in_range = x >= 0 && x < V;
+      // the keep probability, by the thread that holds token x (thread 0 for
+      // an out-of-range token, which is never kept)
+      if (in_range ? tid == x % kThreads : tid == 0) {
+        float a = 0.f;
+        if (in_range) {
+          const int jx = x / kThreads;
+          float px = 0.f;
+#pragma unroll
+          for (int j = 0; j < C; ++j)
+            if (j == jx) px = pv[j];
+          const float qx = s_dist[x];
+          a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
+        }
+        if (keep_prob) keep_prob[(size_t)b * T + c] = a;
+        s_kept = u_node[(size_t)b * T + c] < a ? c : -1;
+      }
+      __syncthreads();
+      kept = s_kept;
+      if (kept >= 0) break;
+      // p <- max(0, p - q) / its sum (p <= q everywhere cannot reject: p stays)
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < C; ++j) part += fmaxf(pv[j] - s_dist[tid + kThreads * j], 0.f);
+      const float Zn = block_sum(part, scr);
+      if (Zn > 0.f) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) pv[j] = fmaxf(pv[j] - s_dist[tid + kThreads * j], 0.f) / Zn;
+      }
+      __syncthreads();
+    }
+    if (kept < 0) break;                                     // all rejected: draw from the residual
+    u = kept;
+    if (tid == 0) path[plen] = u;
+    ++plen;
+  }
+  __syncthreads();   // every thread is done with q
+#pragma unroll
+  for (int j = 0; j < C; ++j) s_dist[tid + kThreads * j] = pv[j];
+  __syncthreads();
+  const int tok = inverse_cdf([&](int v) { return s_dist[v]; }, V, u_bonus[b], s_part, &s_tok, scr);
+  __syncthreads();
+  if (tid == 0) {
+    next_tok[b] = tok;
+    accept_len[b] = depth[u];
+    best_node[b] = u;
+  }
+  for (int i = tid; i < plen; i += kThreads)
+    accepted_tok[(size_t)b * (depth_max + 1) + i] = tree_tok[(size_t)b * T + path[i]];
+}
+
 }  // namespace
 
 extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V, int K,
@@ -309,7 +466,14 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
     s = validate_inputs(as_stream(stream), "rejection_accept", v);
     if (s != MEDUSA_OK) return s;
   }
-  MEDUSA_LAUNCH("rejection_accept", rejection_accept_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V,
+  // vocabularies up to 32768: both distributions in registers; beyond, the
+  // streaming kernel
+  auto kern = V <= kThreads * 4 ? rejection_accept_regs<4>
+            : V <= kThreads * 8 ? rejection_accept_regs<8>
+            : V <= kThreads * 16 ? rejection_accept_regs<16>
+            : V <= kThreads * 32 ? rejection_accept_regs<32>
+                                 : rejection_accept_kernel;
+  MEDUSA_LAUNCH("rejection_accept", kern, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V,
                      t->depth_max, t->d_parent, t->d_depth, t->d_dstart, logits, head_logits, B, tree_tok,
                      temperature, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
   return check_launch("rejection_accept");
