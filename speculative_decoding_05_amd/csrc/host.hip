@@ -45,7 +45,8 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   if (t->d_base) return MEDUSA_OK;
   const size_t T = t->T;
   const size_t mask_b = T * t->W * sizeof(uint64_t);
-  const size_t ints = 4 * T + t->internal.size() + t->dstart.size() + t->tile_need.size();
+  const size_t ints = 4 * T + t->internal.size() + t->dstart.size() + t->tile_need.size() + t->cstart.size() +
+                      t->clist.size();
   const size_t bytes = mask_b + ints * sizeof(int32_t);
   std::vector<unsigned char> img(bytes);
   unsigned char *p = img.data();
@@ -58,8 +59,11 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   std::copy(t->slot.begin(), t->slot.end(), q + 3 * T);
   std::copy(t->internal.begin(), t->internal.end(), q + 4 * T);
   std::copy(t->dstart.begin(), t->dstart.end(), q + 4 * T + t->internal.size());
-  std::copy(t->tile_need.begin(), t->tile_need.end(),
-            reinterpret_cast<uint32_t *>(q + 4 * T + t->internal.size() + t->dstart.size()));
+  int32_t *qc = q + 4 * T + t->internal.size() + t->dstart.size();
+  std::copy(t->tile_need.begin(), t->tile_need.end(), reinterpret_cast<uint32_t *>(qc));
+  qc += t->tile_need.size();
+  std::copy(t->cstart.begin(), t->cstart.end(), qc);
+  std::copy(t->clist.begin(), t->clist.end(), qc + t->cstart.size());
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return fail(MEDUSA_ERR_HIP, "tree_upload: no HIP device");
   void *d = nullptr;
@@ -82,6 +86,8 @@ extern "C" medusa_status medusa_tree_upload(medusa_tree *t) {
   t->d_internal = di + 4 * T;
   t->d_dstart = di + 4 * T + t->internal.size();
   t->d_tile_need = reinterpret_cast<const uint32_t *>(t->d_dstart + t->dstart.size());
+  t->d_cstart = t->d_dstart + t->dstart.size() + t->tile_need.size();
+  t->d_clist = t->d_cstart + t->cstart.size();
   return MEDUSA_OK;
 }
 

@@ -24,6 +24,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxResid = MEDUSA_MAX_TREE;   // rejections at one node <= its children
+constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3 on gfx9: 32-bit elements
 
 struct BlockScratch {
   float f[kWaves];
@@ -278,161 +279,273 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_kernel(
     accepted_tok[(size_t)b * (depth_max + 1) + i] = tree_tok[(size_t)b * T + path[i]];
 }
 
-// The same walk with the distributions held on chip, for V <= 1024 * C: p in
-// registers (thread t owns v = t + 1024 j, j < C, the order in which the
-// streaming kernel above sums, so p, q, every normaliser and every keep
-// probability come out bit for bit the same), q in LDS.  A rejection costs
-// one block sum (the residual is updated in place, never recomputed from the
-// rows), and the final draw scans p from LDS.
+// x, opaque to the optimiser: values derived from it inside a loop are
+// recomputed there (one instruction each) rather than hoisted out of the loop
+// and held in registers across it.  Register-only; no memory is touched.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Block reductions with one barrier each: the wave results go to one of two
+// scratch halves, used in turn.  A thread writes half h again only two calls
+// later, after the barrier of the call in between, which every thread reaches
+// only once it has read half h.  Every thread makes the same calls.
+struct PingPong {
+  float f[2][kWaves];
+  uint64_t k[2][kWaves];
+};
+struct Reducer {
+  PingPong &s;
+  int ph = 0;
+  __device__ float sum(float v) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) s.f[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) r += s.f[ph][w];
+    ph ^= 1;
+    return r;
+  }
+  __device__ float max(float v) {
+    v = wave_maxf(v);
+    if ((threadIdx.x & 63) == 0) s.f[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) r = fmaxf(r, s.f[ph][w]);
+    ph ^= 1;
+    return r;
+  }
+  __device__ uint64_t max_u64(uint64_t v) {
+    v = wave_max_u64(v);
+    if ((threadIdx.x & 63) == 0) s.k[ph][threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint64_t r = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) r = s.k[ph][w] > r ? s.k[ph][w] : r;
+    ph ^= 1;
+    return r;
+  }
+};
+
+// The same walk with the distributions held on chip, for V <= 1024 * C.
+// Thread t holds p(v) for v = t + 1024 j, j < C, in registers; q sits in LDS.
+// Each node's two rows are read once, every load of a row in flight at once
+// (buffer loads, which return 0 past the row's end).  The sequence's tokens
+// and uniforms and the child offsets are copied to LDS at the start, so a
+// node costs one global lookup (its child list) besides its rows.  p at each
+// child's token is gathered into LDS by the thread holding it; every thread
+// then evaluates each keep probability itself (the residual normalisers so
+// far applied to that value), so a decision needs no broadcast, and a
+// rejection costs one block sum, the residual max(0, p - q) / Z replacing p in
+// place.  The final draw stores p in LDS padded by one word per C, so thread
+// t reads its contiguous range [t C, t C + C) without bank conflicts, and
+// scans the range sums with wave shuffles and one pass over the wave totals.
 template <int C>
 __global__ __launch_bounds__(kThreads) void rejection_accept_regs(
-    int T, int V, int depth_max, const int32_t *__restrict__ parent, const int32_t *__restrict__ depth,
-    const int32_t *__restrict__ dstart, const float *__restrict__ logits, const float *__restrict__ head_logits,
+    int T, int V, int depth_max, const int32_t *__restrict__ depth, const int32_t *__restrict__ cstart,
+    const int32_t *__restrict__ clist, const float *__restrict__ logits, const float *__restrict__ head_logits,
     int B, const int32_t *__restrict__ tree_tok, float tau, const float *__restrict__ u_node,
     const float *__restrict__ u_bonus, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
     int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ keep_prob) {
-  __shared__ BlockScratch scr;
+  constexpr int kPad = kThreads * C + kThreads;   // element v at v + v / C
+  __shared__ PingPong pp;
+  __shared__ int s_cstart[MEDUSA_MAX_TREE + 1];
+  __shared__ int s_tok_all[MEDUSA_MAX_TREE];
+  __shared__ float s_u_all[MEDUSA_MAX_TREE];
   __shared__ int cld[MEDUSA_MAX_TREE];
-  __shared__ int path[MEDUSA_MAX_TREE];
-  __shared__ float s_part[kThreads];
-  __shared__ float s_dist[kThreads * C];
-  __shared__ int s_ncld, s_kept, s_tok;
+  __shared__ float cpx[MEDUSA_MAX_TREE];   // p at each child's token before any rejection
+  __shared__ float rZ[kMaxResid];          // 1 / normaliser of each residual so far
+  __shared__ float s_dist[kPad];
+  __shared__ float s_wt[kWaves];
+  __shared__ int s_tok;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
-  if (keep_prob)
-    for (int c = tid; c < T; c += kThreads) keep_prob[(size_t)b * T + c] = __builtin_nanf("");
-  for (int i = tid; i <= depth_max; i += kThreads) accepted_tok[(size_t)b * (depth_max + 1) + i] = -1;
+  const int lane = tid & 63, wave = tid >> 6;
+  Reducer red{pp};
+  auto at = [](int v) { return v + v / C; };
+  constexpr int kStride = kThreads + kThreads / C;   // at(v + 1024) - at(v)
+  const int tat = at(tid);
+  for (int c = tid; c < T; c += kThreads) {
+    s_tok_all[c] = tree_tok[(size_t)b * T + c];
+    s_u_all[c] = u_node[(size_t)b * T + c];
+    if (keep_prob) keep_prob[(size_t)b * T + c] = __builtin_nanf("");
+  }
+  for (int c = tid; c <= T; c += kThreads) s_cstart[c] = cstart[c];
+  for (int i = tid; i <= depth_max; i += kThreads)
+    accepted_tok[(size_t)b * (depth_max + 1) + i] = i == 0 ? tree_tok[(size_t)b * T] : -1;
+  __syncthreads();
 
-  // this thread's values of p over the vocabulary (0 past V)
+  // this thread's values of softmax(row / tau) (one-hot at the argmax for
+  // tau = 0), 0 past V
   auto load_dist = [&](float (&d)[C], const float *row) {
+    // a buffer resource over the row: reads past its V words return 0
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, V * 4, kBufferWord3);
+    auto ld = [&](int v) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, v * 4, 0, 0));
+    };
+    const int t = opaque(tid);
     if (tau == 0.f) {
       uint64_t best = 0;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        const int v = tid + kThreads * j;
-        if (v < V) {
-          const uint64_t key = argmax_key(row[v], v);
-          best = key > best ? key : best;
-        }
+        const int v = t + kThreads * j;
+        const uint64_t key = argmax_key(ld(v), v);
+        best = v < V && key > best ? key : best;
       }
-      const int amax = (int)(~(uint32_t)block_max_u64(best, scr));
+      const int amax = (int)(~(uint32_t)red.max_u64(best));
 #pragma unroll
-      for (int j = 0; j < C; ++j) d[j] = tid + kThreads * j == amax ? 1.f : 0.f;
+      for (int j = 0; j < C; ++j) d[j] = t + kThreads * j == amax ? 1.f : 0.f;
       return;
     }
     const float inv_tau = 1.f / tau;
     float m = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {   // the scaled logits first, in place
-      const int v = tid + kThreads * j;
-      d[j] = v < V ? row[v] * inv_tau : -INFINITY;
+    for (int j = 0; j < C; ++j) {
+      const int v = t + kThreads * j;
+      const float x = ld(v);
+      d[j] = v < V ? x * inv_tau : -INFINITY;
       m = fmaxf(m, d[j]);
     }
-    m = block_max(m, scr);
+    m = red.max(m);
     float S = 0.f;
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      d[j] = tid + kThreads * j < V ? __expf(d[j] - m) : 0.f;
+    for (int j = 0; j < C; ++j) {   // past V: exp(-inf) = 0
+      d[j] = __expf(d[j] - m);
       S += d[j];
     }
-    S = block_sum(S, scr);
+    const float rS = 1.f / red.sum(S);
 #pragma unroll
-    for (int j = 0; j < C; ++j) d[j] = d[j] / S;
-  };
-
-  // q into s_dist (0 past V), by rolled loops: the same values as load_dist
-  auto load_q = [&](const float *row) {
-    if (tau == 0.f) {
-      uint64_t best = 0;
-      for (int v = tid; v < V; v += kThreads) {
-        const uint64_t key = argmax_key(row[v], v);
-        best = key > best ? key : best;
-      }
-      const int amax = (int)(~(uint32_t)block_max_u64(best, scr));
-      for (int v = tid; v < kThreads * C; v += kThreads) s_dist[v] = v == amax ? 1.f : 0.f;
-    } else {
-      const float inv_tau = 1.f / tau;
-      float m = -INFINITY;
-      for (int v = tid; v < V; v += kThreads) m = fmaxf(m, row[v] * inv_tau);
-      m = block_max(m, scr);
-      float S = 0.f;
-      for (int v = tid; v < V; v += kThreads) S += __expf(row[v] * inv_tau - m);
-      S = block_sum(S, scr);
-      for (int v = tid; v < kThreads * C; v += kThreads) s_dist[v] = v < V ? __expf(row[v] * inv_tau - m) / S : 0.f;
-    }
-    __syncthreads();
+    for (int j = 0; j < C; ++j) d[j] *= rS;
   };
 
   float pv[C];
   int u = 0, plen = 1;
-  if (tid == 0) path[0] = 0;
   while (true) {
-    load_dist(pv, logits + ((size_t)b * T + u) * V);
     const int d = depth[u];
-    if (tid == 0) {
-      int n = 0;
-      if (d < depth_max)
-        for (int c = dstart[d + 1]; c < dstart[d + 2]; ++c)
-          if (parent[c] == u) cld[n++] = c;
-      s_ncld = n;
+    const int c0 = s_cstart[u], ncld = s_cstart[u + 1] - c0;
+    for (int i = tid; i < ncld; i += kThreads) cld[i] = clist[c0 + i];
+    // q (when u has children) through the registers into LDS, then p; one
+    // copy of the loads, so the second row's cannot be hoisted over the first
+    // row's reductions and double the registers in use
+#pragma unroll 1
+    for (int r = ncld > 0 ? 0 : 1; r < 2; ++r) {
+      load_dist(pv, r == 0 ? head_logits + ((size_t)d * B + b) * V : logits + ((size_t)b * T + u) * V);
+      if (r == 0) {
+        const int o = opaque(tat);
+#pragma unroll
+        for (int j = 0; j < C; ++j) s_dist[o + kStride * j] = pv[j];
+      }
+    }
+    // the reductions' barriers have published cld and q
+    if (ncld == 0) break;                              // leaf: draw from p
+    for (int i = 0; i < ncld; ++i) {
+      const int x = s_tok_all[cld[i]];
+      if (x >= 0 && x < V && tid == x % kThreads) {
+        const int jx = x / kThreads;
+        float px = 0.f;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+          if (j == jx) px = pv[j];
+        cpx[i] = px;
+      }
     }
     __syncthreads();
-    const int ncld = s_ncld;
-    if (ncld == 0) break;                                   // leaf: draw from p
-    load_q(head_logits + ((size_t)d * B + b) * V);
-    int kept = -1;
+    int kept = -1, nz = 0;
     for (int i = 0; i < ncld; ++i) {
       const int c = cld[i];
-      const int x = tree_tok[(size_t)b * T + c];
-      const bool in_range = x >= 0 && x < V;
-      // the keep probability, by the thread that holds token x (thread 0 for
-      // an out-of-range token, which is never kept)
-      if (in_range ? tid == x % kThreads : tid == 0) {
-        float a = 0.f;
-        if (in_range) {
-          const int jx = x / kThreads;
-          float px = 0.f;
-#pragma unroll
-          for (int j = 0; j < C; ++j)
-            if (j == jx) px = pv[j];
-          const float qx = s_dist[x];
-          a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
-        }
-        if (keep_prob) keep_prob[(size_t)b * T + c] = a;
-        s_kept = u_node[(size_t)b * T + c] < a ? c : -1;
+      const int x = s_tok_all[c];
+      float a = 0.f;                                   // out-of-range tokens are never kept
+      if (x >= 0 && x < V) {
+        const float qx = s_dist[at(x)];
+        float px = cpx[i];
+        for (int j = 0; j < nz; ++j) px = fmaxf(px - qx, 0.f) * rZ[j];
+        a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
       }
-      __syncthreads();
-      kept = s_kept;
-      if (kept >= 0) break;
+      if (tid == 0 && keep_prob) keep_prob[(size_t)b * T + c] = a;
+      if (s_u_all[c] < a) {
+        kept = c;
+        break;
+      }
       // p <- max(0, p - q) / its sum (p <= q everywhere cannot reject: p stays)
       float part = 0.f;
+      const int o = opaque(tat);
 #pragma unroll
-      for (int j = 0; j < C; ++j) part += fmaxf(pv[j] - s_dist[tid + kThreads * j], 0.f);
-      const float Zn = block_sum(part, scr);
+      for (int j = 0; j < C; ++j) part += fmaxf(pv[j] - s_dist[o + kStride * j], 0.f);
+      const float Zn = red.sum(part);
       if (Zn > 0.f) {
+        const float r = 1.f / Zn;
+        const int o2 = opaque(tat);
 #pragma unroll
-        for (int j = 0; j < C; ++j) pv[j] = fmaxf(pv[j] - s_dist[tid + kThreads * j], 0.f) / Zn;
+        for (int j = 0; j < C; ++j) pv[j] = fmaxf(pv[j] - s_dist[o2 + kStride * j], 0.f) * r;
+        rZ[nz] = r;   // by every thread, so each reads back its own write
+        ++nz;
       }
-      __syncthreads();
     }
-    if (kept < 0) break;                                     // all rejected: draw from the residual
+    __syncthreads();   // every thread is done with this node's q, cld and cpx
+    if (kept < 0) break;                               // all rejected: draw from the residual
+    if (tid == 0) accepted_tok[(size_t)b * (depth_max + 1) + plen] = s_tok_all[kept];
     u = kept;
-    if (tid == 0) path[plen] = u;
     ++plen;
   }
-  __syncthreads();   // every thread is done with q
+
+  // inverse-CDF draw from p: the smallest v with p(0) + ... + p(v) > u * sum,
+  // else (rounding) the last v with p(v) > 0
 #pragma unroll
-  for (int j = 0; j < C; ++j) s_dist[tid + kThreads * j] = pv[j];
+  for (int j = 0; j < C; ++j) s_dist[tat + kStride * j] = pv[j];
+  if (tid == 0) s_tok = -1;
   __syncthreads();
-  const int tok = inverse_cdf([&](int v) { return s_dist[v]; }, V, u_bonus[b], s_part, &s_tok, scr);
+  float own = 0.f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) own += s_dist[tid * (C + 1) + i];
+  float incl = own;   // inclusive scan over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  float excl = __shfl_up(incl, 1, 64);
+  if (lane == 0) excl = 0.f;
+  if (lane == 63) s_wt[wave] = incl;
   __syncthreads();
+  float base = 0.f, total = 0.f;
+  for (int w = 0; w < kWaves; ++w) {   // the same running sum for every thread
+    if (w == wave) base = total;
+    total += s_wt[w];
+  }
+  // thread t's share of the running sum is [lo, hi); hi of one thread is lo
+  // of the next bit for bit, so at most one thread claims the target
+  const float lo = base + excl, hi = base + incl;
+  const float target = u_bonus[b] * total;
+  if (hi > lo && target >= lo && target < hi) {
+    float acc = lo;
+    int tok = -1;
+    for (int i = 0; i < C && tok < 0; ++i) {
+      const float x = s_dist[tid * (C + 1) + i];
+      acc += x;
+      if (x > 0.f && acc > target) tok = tid * C + i;
+    }
+    for (int i = C - 1; i >= 0 && tok < 0; --i)
+      if (s_dist[tid * (C + 1) + i] > 0.f) tok = tid * C + i;
+    s_tok = tok;
+  }
+  __syncthreads();
+  int tok = s_tok;
+  if (tok < 0) {
+    int last = -1;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+      if (pv[j] > 0.f) last = tid + kThreads * j;
+    tok = (int)red.max_u64((uint64_t)(uint32_t)(last + 1)) - 1;
+  }
   if (tid == 0) {
     next_tok[b] = tok;
     accept_len[b] = depth[u];
     best_node[b] = u;
   }
-  for (int i = tid; i < plen; i += kThreads)
-    accepted_tok[(size_t)b * (depth_max + 1) + i] = tree_tok[(size_t)b * T + path[i]];
 }
 
 }  // namespace
@@ -468,13 +581,18 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
   }
   // vocabularies up to 32768: both distributions in registers; beyond, the
   // streaming kernel
-  auto kern = V <= kThreads * 4 ? rejection_accept_regs<4>
-            : V <= kThreads * 8 ? rejection_accept_regs<8>
-            : V <= kThreads * 16 ? rejection_accept_regs<16>
-            : V <= kThreads * 32 ? rejection_accept_regs<32>
-                                 : rejection_accept_kernel;
-  MEDUSA_LAUNCH("rejection_accept", kern, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V,
-                     t->depth_max, t->d_parent, t->d_depth, t->d_dstart, logits, head_logits, B, tree_tok,
-                     temperature, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
+  if (V > kThreads * 32) {
+    MEDUSA_LAUNCH("rejection_accept", rejection_accept_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T,
+                  V, t->depth_max, t->d_parent, t->d_depth, t->d_dstart, logits, head_logits, B, tree_tok,
+                  temperature, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
+  } else {
+    auto kern = V <= kThreads * 4 ? rejection_accept_regs<4>
+              : V <= kThreads * 8 ? rejection_accept_regs<8>
+              : V <= kThreads * 16 ? rejection_accept_regs<16>
+                                   : rejection_accept_regs<32>;
+    MEDUSA_LAUNCH("rejection_accept", kern, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V, t->depth_max,
+                  t->d_depth, t->d_cstart, t->d_clist, logits, head_logits, B, tree_tok, temperature, u_node,
+                  u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
+  }
   return check_launch("rejection_accept");
 }

@@ -183,6 +183,14 @@ extern "C" medusa_status medusa_build_tree(const int32_t *ranks, const int32_t *
       t->internal.push_back(j);
     }
   t->n_internal = static_cast<int>(t->internal.size());
+  t->cstart.assign(t->T + 1, 0);
+  for (int j = 1; j < t->T; ++j) ++t->cstart[t->parent[j] + 1];
+  for (int j = 0; j < t->T; ++j) t->cstart[j + 1] += t->cstart[j];
+  t->clist.assign(t->T - 1, 0);
+  {
+    std::vector<int32_t> next(t->cstart.begin(), t->cstart.end() - 1);
+    for (int j = 1; j < t->T; ++j) t->clist[next[t->parent[j]]++] = j;
+  }
   t->depth_max = *std::max_element(t->depth.begin(), t->depth.end());
   t->dstart.assign(t->depth_max + 2, t->T);  // nodes are sorted by depth
   for (int j = t->T - 1; j >= 0; --j) t->dstart[t->depth[j]] = j;

@@ -16,6 +16,9 @@ struct medusa_tree {
   std::vector<int32_t> internal;  // nodes with children, ascending
   std::vector<int32_t> slot;      // node -> index in `internal`, -1 for leaves
   std::vector<int32_t> dstart;    // [depth_max + 2]: nodes of depth d are dstart[d] .. dstart[d+1]-1
+  // children of node u, ascending (rank order): clist[cstart[u] .. cstart[u+1])
+  std::vector<int32_t> cstart;    // [T + 1]
+  std::vector<int32_t> clist;     // [T - 1]
   std::vector<uint64_t> mask;     // [T][W]
   // per group of 16 consecutive nodes: bit w set iff some node of the group
   // has an ancestor (or is itself) among nodes 64w .. 64w+63
@@ -27,6 +30,7 @@ struct medusa_tree {
   const int32_t *d_parent = nullptr, *d_depth = nullptr, *d_rank = nullptr;
   const int32_t *d_internal = nullptr, *d_slot = nullptr, *d_dstart = nullptr;
   const uint32_t *d_tile_need = nullptr;
+  const int32_t *d_cstart = nullptr, *d_clist = nullptr;
 };
 
 namespace medusa {

@@ -18,6 +18,10 @@ CDF_BAND = 1e-4   # draws whose target lies this close (relative) to a CDF step 
 def make_tree(kind):
     if kind == "greedy64":
         p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10
+    elif kind == "greedy1024":   # the largest tree (1024 nodes)
+        p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 1023, 10), 4, 10
+    elif kind == "star50":       # one node with 50 children: long runs of rejections
+        p, K, k = [[i] for i in range(50)], 1, 50
     elif kind == "dense33":
         p, K, k = oracle.dense_paths(3, 3), 3, 3
     else:
@@ -80,6 +84,11 @@ def run_gpu(t, vl, head, tok, tau, u_node, u_bonus, depth_max):
     ("dense33", 6, 1000, 1.0), ("dense33", 6, 1000, 0.7), ("greedy64", 4, 32000, 1.0),
     ("greedy64", 4, 5003, 1.5), ("chain5", 5, 777, 1.0), ("dense33", 4, 1000, 0.0),
     ("greedy64", 3, 32000, 0.0),
+    ("greedy64", 3, 32768, 1.0),     # the largest vocabulary held on chip
+    ("greedy64", 2, 40000, 1.0),     # beyond it: the streaming kernel
+    ("greedy64", 2, 40000, 0.0),
+    ("star50", 6, 3000, 1.0), ("star50", 4, 20000, 2.0),
+    ("greedy1024", 3, 32000, 1.0), ("greedy1024", 2, 1500, 0.0),
 ])
 def test_rejection_accept_parity(kind, B, V, tau):
     say("rejection", kind, B, V, tau)
