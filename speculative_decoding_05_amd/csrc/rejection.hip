@@ -7,12 +7,15 @@
 // below min(1, p(x)/q(x)), and a rejected child replaces p by the
 // renormalised residual max(0, p - q) -- and moves to the first kept child.
 // When no child is kept, or u is a leaf, the next token is drawn by inverse
-// CDF from the current p.
+// CDF from the current p.  Temperature 0 uses one-hot distributions at the
+// argmax (lowest index): greedy verification.
 //
-// The residual after j rejections is never stored: every pass recomputes it
-// per element from p(v), q(v) and the j normalisers, so the block only streams
-// the two rows (L2-resident after the first pass).  Temperature 0 uses
-// one-hot distributions at the argmax (lowest index): greedy verification.
+// Vocabularies up to 32768 hold p in registers and q in LDS
+// (rejection_accept_regs); larger ones stream the two rows from L2
+// (rejection_accept_stream).  Both read a row with buffer loads, all of a
+// thread's loads in flight together, and stage the sequence's tokens,
+// uniforms and the tree's child offsets in LDS, so the walk itself makes no
+// dependent global loads beyond each node's child list and rows.
 #include <math.h>
 
 #include "common.h"
@@ -25,11 +28,6 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxResid = MEDUSA_MAX_TREE;   // rejections at one node <= its children
 constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3 on gfx9: 32-bit elements
-
-struct BlockScratch {
-  float f[kWaves];
-  uint64_t k[kWaves];
-};
 
 __device__ __forceinline__ float wave_sum(float v) {
   v += dppf<kDppXor1>(v);
@@ -56,227 +54,11 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return r;
 }
 
-// block-wide reductions; every thread gets the result
-__device__ float block_sum(float v, BlockScratch &s) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s.f[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) r += s.f[w];
-  return r;
-}
-__device__ float block_max(float v, BlockScratch &s) {
-  v = wave_maxf(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s.f[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) r = fmaxf(r, s.f[w]);
-  return r;
-}
-__device__ uint64_t block_max_u64(uint64_t v, BlockScratch &s) {
-  v = wave_max_u64(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s.k[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint64_t r = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) r = s.k[w] > r ? s.k[w] : r;
-  return r;
-}
-
 // argmax key: larger value first, then smaller index
 __device__ __forceinline__ uint64_t argmax_key(float x, int i) {
   uint32_t u = __builtin_bit_cast(uint32_t, x == 0.f ? 0.f : x);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((uint64_t)u << 32) | (uint32_t)(~(uint32_t)i);
-}
-
-// A distribution over the vocabulary: softmax(row / tau), or one-hot at amax
-struct Dist {
-  const float *row;
-  float m = 0.f, S = 1.f, inv_tau = 0.f;
-  int amax = 0;  // >= 0: one-hot
-  __device__ float operator()(int v) const {
-    if (amax >= 0) return v == amax ? 1.f : 0.f;
-    return __expf((row[v] * inv_tau - m)) / S;
-  }
-};
-
-__device__ Dist make_dist(const float *row, int V, float tau, BlockScratch &s) {
-  Dist d;
-  d.row = row;
-  if (tau == 0.f) {
-    uint64_t best = 0;
-    for (int v = threadIdx.x; v < V; v += kThreads) {
-      const uint64_t key = argmax_key(row[v], v);
-      best = key > best ? key : best;
-    }
-    best = block_max_u64(best, s);
-    d.amax = (int)(~(uint32_t)best);
-    d.m = 0.f;
-    d.S = 1.f;
-    d.inv_tau = 0.f;
-    return d;
-  }
-  d.amax = -1;
-  d.inv_tau = 1.f / tau;
-  float m = -INFINITY;
-  for (int v = threadIdx.x; v < V; v += kThreads) m = fmaxf(m, row[v] * d.inv_tau);
-  d.m = block_max(m, s);
-  float S = 0.f;
-  for (int v = threadIdx.x; v < V; v += kThreads) S += __expf(row[v] * d.inv_tau - d.m);
-  d.S = block_sum(S, s);
-  return d;
-}
-
-// p after the rejections recorded in Z[0..nz): p_{j+1} = max(0, p_j - q) / Z[j]
-__device__ __forceinline__ float residual(float p, float q, const float *Z, int nz) {
-  for (int j = 0; j < nz; ++j) p = fmaxf(p - q, 0.f) / Z[j];
-  return p;
-}
-
-// Inverse-CDF draw: the smallest v with f(0) + ... + f(v) > u * sum(f), or the
-// last v with f(v) > 0 if rounding leaves none.  Thread t owns the contiguous
-// range [t*C, (t+1)*C); a block scan of the 1024 range sums finds the range
-// that holds the target.  Every thread gets the token.
-template <typename F>
-__device__ int inverse_cdf(const F &f, int V, float u, float *s_part, int *s_tok, BlockScratch &scr) {
-  const int tid = threadIdx.x;
-  const int C = (V + kThreads - 1) / kThreads;
-  const int v0 = min(V, tid * C), v1 = min(V, v0 + C);
-  float own = 0.f;
-  for (int v = v0; v < v1; ++v) own += f(v);
-  __syncthreads();
-  s_part[tid] = own;
-  if (tid == 0) *s_tok = -1;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {   // inclusive scan (Hillis-Steele)
-    const float add = tid >= off ? s_part[tid - off] : 0.f;
-    __syncthreads();
-    s_part[tid] += add;
-    __syncthreads();
-  }
-  // thread t's range of the running sum is [s_part[t-1], s_part[t]): the
-  // ranges are disjoint, so at most one thread claims the target
-  const float target = u * s_part[kThreads - 1];
-  const float lo = tid > 0 ? s_part[tid - 1] : 0.f, hi = s_part[tid];
-  if (hi > lo && target >= lo && target < hi) {
-    float acc = lo;
-    int tok = -1;
-    for (int v = v0; v < v1 && tok < 0; ++v) {
-      const float pv = f(v);
-      acc += pv;
-      if (pv > 0.f && acc > target) tok = v;
-    }
-    for (int v = v1 - 1; v >= v0 && tok < 0; --v)
-      if (f(v) > 0.f) tok = v;
-    *s_tok = tok;
-  }
-  __syncthreads();
-  int tok = *s_tok;
-  if (tok < 0) {
-    int last = -1;
-    for (int v = tid; v < V; v += kThreads)
-      if (f(v) > 0.f) last = v;
-    tok = (int)block_max_u64((uint64_t)(uint32_t)(last + 1), scr) - 1;
-  }
-  return tok;
-}
-
-__global__ __launch_bounds__(kThreads) void rejection_accept_kernel(
-    int T, int V, int depth_max, const int32_t *__restrict__ parent, const int32_t *__restrict__ depth,
-    const int32_t *__restrict__ dstart, const float *__restrict__ logits, const float *__restrict__ head_logits,
-    int B, const int32_t *__restrict__ tree_tok, float tau, const float *__restrict__ u_node,
-    const float *__restrict__ u_bonus, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
-    int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ keep_prob) {
-  __shared__ BlockScratch scr;
-  __shared__ int cld[MEDUSA_MAX_TREE];
-  __shared__ float Z[kMaxResid];
-  __shared__ int path[MEDUSA_MAX_TREE];
-  __shared__ float s_part[kThreads];
-  __shared__ int s_ncld, s_kept, s_tok;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (keep_prob)
-    for (int c = tid; c < T; c += kThreads) keep_prob[(size_t)b * T + c] = __builtin_nanf("");
-  for (int i = tid; i <= depth_max; i += kThreads) accepted_tok[(size_t)b * (depth_max + 1) + i] = -1;
-
-  int u = 0, plen = 1, nz = 0;
-  if (tid == 0) path[0] = 0;
-  Dist p, q;
-  q.row = nullptr;
-  bool resid = false;   // the final draw is from the residual of u's rejected children
-  while (true) {
-    p = make_dist(logits + ((size_t)b * T + u) * V, V, tau, scr);
-    const int d = depth[u];
-    if (tid == 0) {
-      int n = 0;
-      if (d < depth_max)
-        for (int c = dstart[d + 1]; c < dstart[d + 2]; ++c)
-          if (parent[c] == u) cld[n++] = c;
-      s_ncld = n;
-    }
-    __syncthreads();
-    const int ncld = s_ncld;
-    nz = 0;
-    if (ncld == 0) break;                                   // leaf: draw from p
-    q = make_dist(head_logits + ((size_t)d * B + b) * V, V, tau, scr);
-    int kept = -1;
-    for (int i = 0; i < ncld; ++i) {
-      const int c = cld[i];
-      if (tid == 0) {
-        const int x = tree_tok[(size_t)b * T + c];
-        float a = 0.f;                                      // out-of-range tokens are never kept
-        if (x >= 0 && x < V) {
-          const float qx = q(x), px = residual(p(x), qx, Z, nz);
-          a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
-        }
-        if (keep_prob) keep_prob[(size_t)b * T + c] = a;
-        s_kept = u_node[(size_t)b * T + c] < a ? c : -1;
-      }
-      __syncthreads();
-      kept = s_kept;
-      if (kept >= 0) break;
-      // normaliser of the residual max(0, p_nz - q) after this rejection
-      float part = 0.f;
-      for (int v = tid; v < V; v += kThreads) {
-        const float qv = q(v);
-        part += fmaxf(residual(p(v), qv, Z, nz) - qv, 0.f);
-      }
-      const float Zn = block_sum(part, scr);
-      if (Zn > 0.f) {   // p <= q everywhere cannot reject: p stays
-        if (tid == 0) Z[nz] = Zn;
-        ++nz;
-      }
-      __syncthreads();
-    }
-    if (kept < 0) {                                          // all rejected
-      resid = nz > 0;
-      break;
-    }
-    u = kept;
-    if (tid == 0) path[plen] = u;
-    ++plen;
-  }
-  int tok;
-  if (resid) {
-    tok = inverse_cdf([&](int v) { const float qv = q(v); return residual(p(v), qv, Z, nz); }, V, u_bonus[b],
-                      s_part, &s_tok, scr);
-  } else {
-    tok = inverse_cdf([&](int v) { return p(v); }, V, u_bonus[b], s_part, &s_tok, scr);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    next_tok[b] = tok;
-    accept_len[b] = depth[u];
-    best_node[b] = u;
-  }
-  for (int i = tid; i < plen; i += kThreads)
-    accepted_tok[(size_t)b * (depth_max + 1) + i] = tree_tok[(size_t)b * T + path[i]];
 }
 
 // x, opaque to the optimiser: values derived from it inside a loop are
@@ -285,6 +67,17 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_kernel(
 __device__ __forceinline__ int opaque(int x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// A value every lane of the wave holds alike (read from LDS, or a block
+// reduction's result), marked uniform for the compiler: branches on it stay
+// scalar, and addresses built from it stay in scalar registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ uint64_t uni(uint64_t x) {
+  return ((uint64_t)(uint32_t)uni((int)(x >> 32)) << 32) | (uint32_t)uni((int)(uint32_t)x);
 }
 
 // Block reductions with one barrier each: the wave results go to one of two
@@ -306,7 +99,7 @@ struct Reducer {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) r += s.f[ph][w];
     ph ^= 1;
-    return r;
+    return uni(r);
   }
   __device__ float max(float v) {
     v = wave_maxf(v);
@@ -316,7 +109,7 @@ struct Reducer {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) r = fmaxf(r, s.f[ph][w]);
     ph ^= 1;
-    return r;
+    return uni(r);
   }
   __device__ uint64_t max_u64(uint64_t v) {
     v = wave_max_u64(v);
@@ -326,7 +119,7 @@ struct Reducer {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) r = s.k[ph][w] > r ? s.k[ph][w] : r;
     ph ^= 1;
-    return r;
+    return uni(r);
   }
 };
 
@@ -426,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_regs(
   int u = 0, plen = 1;
   while (true) {
     const int d = depth[u];
-    const int c0 = s_cstart[u], ncld = s_cstart[u + 1] - c0;
+    const int c0 = uni(s_cstart[u]), ncld = uni(s_cstart[u + 1]) - c0;
     for (int i = tid; i < ncld; i += kThreads) cld[i] = clist[c0 + i];
     // q (when u has children) through the registers into LDS, then p; one
     // copy of the loads, so the second row's cannot be hoisted over the first
@@ -456,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_regs(
     __syncthreads();
     int kept = -1, nz = 0;
     for (int i = 0; i < ncld; ++i) {
-      const int c = cld[i];
-      const int x = s_tok_all[c];
+      const int c = uni(cld[i]);
+      const int x = uni(s_tok_all[c]);
       float a = 0.f;                                   // out-of-range tokens are never kept
       if (x >= 0 && x < V) {
         const float qx = s_dist[at(x)];
@@ -466,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_regs(
         a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
       }
       if (tid == 0 && keep_prob) keep_prob[(size_t)b * T + c] = a;
-      if (s_u_all[c] < a) {
+      if (uni(s_u_all[c]) < uni(a)) {
         kept = c;
         break;
       }
@@ -533,12 +326,319 @@ __global__ __launch_bounds__(kThreads) void rejection_accept_regs(
     s_tok = tok;
   }
   __syncthreads();
-  int tok = s_tok;
+  int tok = uni(s_tok);
   if (tok < 0) {
     int last = -1;
 #pragma unroll
     for (int j = 0; j < C; ++j)
       if (pv[j] > 0.f) last = tid + kThreads * j;
+    tok = (int)red.max_u64((uint64_t)(uint32_t)(last + 1)) - 1;
+  }
+  if (tid == 0) {
+    next_tok[b] = tok;
+    accept_len[b] = depth[u];
+    best_node[b] = u;
+  }
+}
+
+// Vocabularies beyond what a block holds on chip: the same walk with the two
+// rows of a node streamed (L2-resident after the first pass): one pass per
+// distribution, 32 loads in flight per thread.  p and q at the children's tokens are
+// gathered in parallel; the residual after j rejections is recomputed per
+// element from p, q and the j normalisers, with the same arithmetic as the
+// keep probabilities.  The final draw makes one pass over tiles of kTile
+// values (each thread sums a contiguous run of kStreamU values of a tile
+// staged in LDS; a wave scan and the wave totals give each tile's sum, one
+// barrier per tile) and rescans the one tile that holds the target.
+constexpr int kStreamU = 8;
+constexpr int kTile = kThreads * kStreamU;
+constexpr int kTilePad = kTile + kThreads;   // local index l at l + l / kStreamU
+constexpr int kMaxTiles = 1024;              // V <= 8 Mi
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float *row, int V) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(row), (short)0, V * 4, kBufferWord3);
+}
+__device__ __forceinline__ float ldb(__amdgpu_buffer_rsrc_t rs, int v) {   // 0 past the row
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, v * 4, 0, 0));
+}
+
+// softmax(row / tau) (amax < 0) or one-hot at amax
+struct RowDist {
+  __amdgpu_buffer_rsrc_t rs;
+  float m, rS, inv_tau;
+  int amax;
+  __device__ float e(float x) const { return __expf(x * inv_tau - m); }
+  __device__ float at(float x, int v) const { return amax >= 0 ? (v == amax ? 1.f : 0.f) : e(x) * rS; }
+};
+
+// f(v, x) for each v < V this thread visits (v = tid + 1024 i), x = row[v];
+// N loads in flight per thread (N = 32: 128 KB per block, about what one
+// round trip to L2 or HBM takes at a CU's share of the bandwidth)
+template <int N, typename F>
+__device__ __forceinline__ void stream1(__amdgpu_buffer_rsrc_t rs, int V, F f) {
+  const int t = opaque((int)threadIdx.x);
+  for (int v0 = t; v0 < V; v0 += kThreads * N) {
+    float x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = ldb(rs, v0 + kThreads * i);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (v0 + kThreads * i < V) f(v0 + kThreads * i, x[i]);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void stream2(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, int V, F f) {
+  const int t = opaque((int)threadIdx.x);
+  for (int v0 = t; v0 < V; v0 += kThreads * N) {
+    float x[N], y[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      x[i] = ldb(ra, v0 + kThreads * i);
+      y[i] = ldb(rb, v0 + kThreads * i);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (v0 + kThreads * i < V) f(v0 + kThreads * i, x[i], y[i]);
+  }
+}
+constexpr int kOne = 32, kTwo = 16;   // loads in flight per thread: one row, two rows
+
+// One pass over the row: each thread keeps a running max m of row/tau and
+// the sum S of e^(y - m) over its values, rescaled when m grows; the block
+// then merges the (m, S) pairs.
+__device__ RowDist make_rowdist(const float *row, int V, float tau, Reducer &red) {
+  RowDist d;
+  d.rs = row_rsrc(row, V);
+  d.amax = -1;
+  d.m = 0.f;
+  d.rS = 1.f;
+  d.inv_tau = 0.f;
+  if (tau == 0.f) {
+    uint64_t best = 0;
+    stream1<kOne>(d.rs, V, [&](int v, float x) {
+      const uint64_t k = argmax_key(x, v);
+      best = k > best ? k : best;
+    });
+    d.amax = (int)(~(uint32_t)red.max_u64(best));
+    return d;
+  }
+  d.inv_tau = 1.f / tau;
+  float m = -INFINITY, S = 0.f;
+  stream1<kOne>(d.rs, V, [&](int, float x) {
+    const float y = x * d.inv_tau;
+    if (y > -INFINITY) {   // a -inf logit adds nothing
+      const float mn = fmaxf(m, y);
+      S = S * __expf(m - mn) + __expf(y - mn);
+      m = mn;
+    }
+  });
+  d.m = red.max(m);
+  d.rS = 1.f / red.sum(m > -INFINITY ? S * __expf(m - d.m) : 0.f);
+  return d;
+}
+
+// p after the rejections whose reciprocal normalisers are rZ[0..nz)
+__device__ __forceinline__ float residual(float p, float q, const float *rZ, int nz) {
+  for (int j = 0; j < nz; ++j) p = fmaxf(p - q, 0.f) * rZ[j];
+  return p;
+}
+
+__global__ __launch_bounds__(kThreads) void rejection_accept_stream(
+    int T, int V, int depth_max, const int32_t *__restrict__ depth, const int32_t *__restrict__ cstart,
+    const int32_t *__restrict__ clist, const float *__restrict__ logits, const float *__restrict__ head_logits,
+    int B, const int32_t *__restrict__ tree_tok, float tau, const float *__restrict__ u_node,
+    const float *__restrict__ u_bonus, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
+    int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ keep_prob) {
+  __shared__ PingPong pp;
+  __shared__ int s_cstart[MEDUSA_MAX_TREE + 1];
+  __shared__ int s_tok_all[MEDUSA_MAX_TREE];
+  __shared__ float s_u_all[MEDUSA_MAX_TREE];
+  __shared__ int cld[MEDUSA_MAX_TREE];
+  __shared__ float cpx[MEDUSA_MAX_TREE], cqx[MEDUSA_MAX_TREE];   // p and q at each child's token
+  __shared__ float rZ[kMaxResid];
+  __shared__ float s_tile[2][kTilePad];
+  __shared__ float s_wt[2][kWaves];
+  __shared__ float s_base[kMaxTiles + 1];   // running sum of the final distribution before each tile
+  __shared__ int s_tok, s_kstar;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  Reducer red{pp};
+  for (int c = tid; c < T; c += kThreads) {
+    s_tok_all[c] = tree_tok[(size_t)b * T + c];
+    s_u_all[c] = u_node[(size_t)b * T + c];
+    if (keep_prob) keep_prob[(size_t)b * T + c] = __builtin_nanf("");
+  }
+  for (int c = tid; c <= T; c += kThreads) s_cstart[c] = cstart[c];
+  for (int i = tid; i <= depth_max; i += kThreads)
+    accepted_tok[(size_t)b * (depth_max + 1) + i] = i == 0 ? tree_tok[(size_t)b * T] : -1;
+  __syncthreads();
+
+  RowDist P, Q;
+  int u = 0, plen = 1, nz = 0;
+  while (true) {
+    const int d = depth[u];
+    const int c0 = uni(s_cstart[u]), ncld = uni(s_cstart[u + 1]) - c0;
+    for (int i = tid; i < ncld; i += kThreads) cld[i] = clist[c0 + i];
+    P = make_rowdist(logits + ((size_t)b * T + u) * V, V, tau, red);   // its barriers publish cld
+    Q = P;
+    nz = 0;
+    if (ncld == 0) break;                                               // leaf: draw from p
+    Q = make_rowdist(head_logits + ((size_t)d * B + b) * V, V, tau, red);
+    for (int i = tid; i < ncld; i += kThreads) {
+      const int x = s_tok_all[cld[i]];
+      const bool in = x >= 0 && x < V;
+      cpx[i] = in ? P.at(ldb(P.rs, x), x) : 0.f;
+      cqx[i] = in ? Q.at(ldb(Q.rs, x), x) : 0.f;
+    }
+    __syncthreads();
+    int kept = -1;
+    for (int i = 0; i < ncld; ++i) {
+      const int c = uni(cld[i]);
+      const int x = uni(s_tok_all[c]);
+      float a = 0.f;                                                    // out-of-range tokens are never kept
+      if (x >= 0 && x < V) {
+        const float qx = cqx[i], px = residual(cpx[i], qx, rZ, nz);
+        a = qx == 0.f ? (px > 0.f ? 1.f : 0.f) : fminf(1.f, px / qx);
+      }
+      if (tid == 0 && keep_prob) keep_prob[(size_t)b * T + c] = a;
+      if (uni(s_u_all[c]) < uni(a)) {
+        kept = c;
+        break;
+      }
+      float part = 0.f;
+      stream2<kTwo>(P.rs, Q.rs, V, [&](int v, float xp, float xq) {
+        const float qv = Q.at(xq, v);
+        part += fmaxf(residual(P.at(xp, v), qv, rZ, nz) - qv, 0.f);
+      });
+      const float Zn = red.sum(part);
+      if (Zn > 0.f) {   // p <= q everywhere cannot reject: p stays
+        rZ[nz] = 1.f / Zn;   // by every thread, so each reads back its own write
+        ++nz;
+      }
+    }
+    __syncthreads();   // every thread is done with this node's cld, cpx, cqx
+    if (kept < 0) break;                                                // all rejected: the residual
+    if (tid == 0) accepted_tok[(size_t)b * (depth_max + 1) + plen] = s_tok_all[kept];
+    u = kept;
+    ++plen;
+  }
+
+  // the final distribution, f(v) = residual of p after nz rejections (p itself when nz = 0)
+  auto f = [&](int v, float xp, float xq) {
+    const float p = P.at(xp, v);
+    return nz > 0 ? residual(p, Q.at(xq, v), rZ, nz) : p;
+  };
+  const int ntiles = (V + kTile - 1) / kTile;
+  // tile k's raw values (thread t: v = k kTile + 1024 i + t), then f of them
+  // into s_tile[h]; split so that a tile's loads are in flight while the
+  // tile before it is scanned
+  float xr[kStreamU], yr[kStreamU];
+  auto load_tile = [&](int k) {
+    const int v0 = k * kTile + tid;
+#pragma unroll
+    for (int i = 0; i < kStreamU; ++i) {
+      xr[i] = ldb(P.rs, v0 + kThreads * i);
+      yr[i] = nz > 0 ? ldb(Q.rs, v0 + kThreads * i) : 0.f;
+    }
+  };
+  auto put_tile = [&](int k, int h) {
+    const int v0 = k * kTile + tid;
+#pragma unroll
+    for (int i = 0; i < kStreamU; ++i) {
+      const int l = tid + kThreads * i, v = v0 + kThreads * i;
+      s_tile[h][l + l / kStreamU] = v < V ? f(v, xr[i], yr[i]) : 0.f;
+    }
+  };
+  // thread t's run [t U, t U + U) of the staged tile: its sum and the
+  // inclusive scan of the sums over the wave; lane 63 posts the wave total
+  auto scan = [&](int h, float &own, float &incl) {
+    own = 0.f;
+#pragma unroll
+    for (int i = 0; i < kStreamU; ++i) own += s_tile[h][tid * (kStreamU + 1) + i];
+    incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) s_wt[h][wave] = incl;
+  };
+  // a tile's sum: its wave totals added in wave order, the order in which
+  // pass 2 forms each thread's running sum inside the tile, so the tile's last
+  // upper bound there equals the next tile's base exactly
+  auto tile_total = [&](int h) {
+    float t = 0.f;
+    for (int w = 0; w < kWaves; ++w) t += s_wt[h][w];
+    return t;
+  };
+  // pass 1: every tile's sum, one barrier per tile (buffers used in turn)
+  float run = 0.f;
+  if (tid == 0) s_base[0] = 0.f;
+  load_tile(0);
+  put_tile(0, 0);
+  if (ntiles > 1) load_tile(1);
+  for (int k = 0; k < ntiles; ++k) {
+    const int h = k & 1;
+    __syncthreads();
+    if (k > 0) {   // tile k-1's wave totals are complete
+      run += tile_total(h ^ 1);
+      if (tid == 0) s_base[k] = run;
+    }
+    float own, incl;
+    scan(h, own, incl);
+    if (k + 1 < ntiles) {
+      put_tile(k + 1, h ^ 1);
+      if (k + 2 < ntiles) load_tile(k + 2);
+    }
+  }
+  __syncthreads();
+  run += tile_total((ntiles - 1) & 1);
+  if (tid == 0) {
+    s_base[ntiles] = run;
+    s_kstar = -1;
+    s_tok = -1;
+  }
+  __syncthreads();
+  const float total = run, target = u_bonus[b] * total;
+  for (int k = tid; k < ntiles; k += kThreads)
+    if (s_base[k + 1] > s_base[k] && target >= s_base[k] && target < s_base[k + 1]) s_kstar = k;
+  __syncthreads();
+  const int ks = uni(s_kstar);
+  if (ks >= 0) {   // pass 2: rescan the tile that holds the target
+    load_tile(ks);
+    put_tile(ks, 0);
+    __syncthreads();
+    float own, incl;
+    scan(0, own, incl);
+    float excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.f;
+    __syncthreads();
+    float wb = 0.f;
+    for (int w = 0; w < wave; ++w) wb += s_wt[0][w];
+    // the same running sums as pass 1: hi of one thread is lo of the next, and
+    // the tile's last hi is s_base[ks + 1]
+    const float lo = s_base[ks] + (wb + excl), hi = s_base[ks] + (wb + incl);
+    if (hi > lo && target >= lo && target < hi) {
+      float acc = lo;
+      int tok = -1;
+      for (int i = 0; i < kStreamU && tok < 0; ++i) {
+        const float x = s_tile[0][tid * (kStreamU + 1) + i];
+        acc += x;
+        if (x > 0.f && acc > target) tok = ks * kTile + tid * kStreamU + i;
+      }
+      for (int i = kStreamU - 1; i >= 0 && tok < 0; --i)
+        if (s_tile[0][tid * (kStreamU + 1) + i] > 0.f) tok = ks * kTile + tid * kStreamU + i;
+      s_tok = tok;
+    }
+    __syncthreads();
+  }
+  int tok = uni(s_tok);
+  if (tok < 0) {   // rounding left the target past every run: the last v with f(v) > 0
+    int last = -1;
+    stream2<kTwo>(P.rs, Q.rs, V, [&](int v, float xp, float xq) {
+      if (f(v, xp, xq) > 0.f) last = v;
+    });
     tok = (int)red.max_u64((uint64_t)(uint32_t)(last + 1)) - 1;
   }
   if (tid == 0) {
@@ -559,6 +659,8 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
   medusa_status s = check_tree_on_device(t);
   if (s != MEDUSA_OK) return s;
   if (B < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "rejection_accept: B=%d V=%d", B, V);
+  if (V > kMaxTiles * kTile)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "rejection_accept: V=%d > %d", V, kMaxTiles * kTile);
   if (K < t->depth_max)
     return fail(MEDUSA_ERR_SHAPE, "rejection_accept: %d heads for a tree of depth %d", K, t->depth_max);
   if (!(temperature >= 0.f) || !isfinite(temperature))
@@ -579,20 +681,14 @@ extern "C" medusa_status rejection_accept(medusa_stream_t stream, const medusa_t
     s = validate_inputs(as_stream(stream), "rejection_accept", v);
     if (s != MEDUSA_OK) return s;
   }
-  // vocabularies up to 32768: both distributions in registers; beyond, the
-  // streaming kernel
-  if (V > kThreads * 32) {
-    MEDUSA_LAUNCH("rejection_accept", rejection_accept_kernel, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T,
-                  V, t->depth_max, t->d_parent, t->d_depth, t->d_dstart, logits, head_logits, B, tree_tok,
-                  temperature, u_node, u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
-  } else {
-    auto kern = V <= kThreads * 4 ? rejection_accept_regs<4>
-              : V <= kThreads * 8 ? rejection_accept_regs<8>
-              : V <= kThreads * 16 ? rejection_accept_regs<16>
-                                   : rejection_accept_regs<32>;
-    MEDUSA_LAUNCH("rejection_accept", kern, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V, t->depth_max,
-                  t->d_depth, t->d_cstart, t->d_clist, logits, head_logits, B, tree_tok, temperature, u_node,
-                  u_bonus, accept_len, best_node, next_tok, accepted_tok, keep_prob);
-  }
+  // vocabularies up to 32768: p in registers, q in LDS; beyond, the rows streamed
+  auto kern = V <= kThreads * 4 ? rejection_accept_regs<4>
+            : V <= kThreads * 8 ? rejection_accept_regs<8>
+            : V <= kThreads * 16 ? rejection_accept_regs<16>
+            : V <= kThreads * 32 ? rejection_accept_regs<32>
+                                 : rejection_accept_stream;
+  MEDUSA_LAUNCH("rejection_accept", kern, dim3(B), dim3(kThreads), 0, as_stream(stream), t->T, V, t->depth_max,
+                t->d_depth, t->d_cstart, t->d_clist, logits, head_logits, B, tree_tok, temperature, u_node, u_bonus,
+                accept_len, best_node, next_tok, accepted_tok, keep_prob);
   return check_launch("rejection_accept");
 }

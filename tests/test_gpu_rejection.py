@@ -86,7 +86,8 @@ def run_gpu(t, vl, head, tok, tau, u_node, u_bonus, depth_max):
     ("greedy64", 3, 32000, 0.0),
     ("greedy64", 3, 32768, 1.0),     # the largest vocabulary held on chip
     ("greedy64", 2, 40000, 1.0),     # beyond it: the streaming kernel
-    ("greedy64", 2, 40000, 0.0),
+    ("greedy64", 2, 40000, 0.0), ("greedy64", 2, 128256, 1.0), ("star50", 3, 70000, 1.0),
+    ("dense33", 3, 65537, 0.0),
     ("star50", 6, 3000, 1.0), ("star50", 4, 20000, 2.0),
     ("greedy1024", 3, 32000, 1.0), ("greedy1024", 2, 1500, 0.0),
 ])
