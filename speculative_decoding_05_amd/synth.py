@@ -135,7 +135,8 @@ def verification_logits(cfg_id, V, parent, depth, rank, topk_idx, root_tok, acc,
         children other than rank i*, with probability
         p2 = min(exp(U(ln 1e-4, ln 0.3)), 0.9 (1 - r - p1));
       * a distractor token t3 (not the root token, t1, t2, nor any child of
-        n) takes the remaining mass max(1 - r - p1 - p2, 1e-12);
+        n) takes the remaining mass max(1 - r - p1 - p2, 1e-12), when the
+        vocabulary holds such a token;
       * finally a row offset U(-5, 5).
     parent/depth/rank: node arrays of the tree; topk_idx [K][B][k];
     root_tok [B]; acc(d, i) -> float.
@@ -182,12 +183,13 @@ def verification_logits(cfg_id, V, parent, depth, rank, topk_idx, root_tok, acc,
                     t2 = int(topk_idx[d, b, j])
                     planted.append((t2, p2))
                     excl.add(t2)
-            while True:
-                t3 = int(g.integers(V))
-                if t3 not in excl:
-                    break
-            p3 = max(1.0 - r - p1 - p2, 1e-12)
-            planted.append((t3, p3))
+            if len(excl) < V:   # a vocabulary this small may have no token left for it
+                while True:
+                    t3 = int(g.integers(V))
+                    if t3 not in excl:
+                        break
+                p3 = max(1.0 - r - p1 - p2, 1e-12)
+                planted.append((t3, p3))
             for t, p in planted:
                 z[t] = math.log(p)
             z += g.uniform(-5.0, 5.0)

@@ -20,6 +20,8 @@ def make_tree(kind):
         p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 63, 10), 4, 10
     elif kind == "greedy1024":   # the largest tree (1024 nodes)
         p, K, k = oracle.greedy_paths(configs.acc_exact, 4, 1023, 10), 4, 10
+    elif kind == "root":         # the root alone: the walk starts at a leaf
+        p, K, k = [], 1, 1
     elif kind == "star50":       # one node with 50 children: long runs of rejections
         p, K, k = [[i] for i in range(50)], 1, 50
     elif kind == "dense33":
@@ -90,6 +92,7 @@ def run_gpu(t, vl, head, tok, tau, u_node, u_bonus, depth_max):
     ("dense33", 3, 65537, 0.0),
     ("star50", 6, 3000, 1.0), ("star50", 4, 20000, 2.0),
     ("greedy1024", 3, 32000, 1.0), ("greedy1024", 2, 1500, 0.0),
+    ("root", 3, 1, 1.0), ("root", 4, 3000, 0.0), ("root", 2, 50000, 0.7),
 ])
 def test_rejection_accept_parity(kind, B, V, tau):
     say("rejection", kind, B, V, tau)
