@@ -369,7 +369,7 @@ medusa_status typical_accept_noalloc(medusa_stream_t stream, const medusa_tree *
  *  accept_len, best_node, next_tok [B], accepted_tok [B][depth_max+1]: as
  *  typical_accept.  keep_prob [B][T] device float, optional (NULL): the
  *  keep probability of every tried child, nan elsewhere.
- *  Errors: ERR_SHAPE (K < depth_max), ERR_ARG. */
+ *  Errors: ERR_SHAPE (K < depth_max), ERR_ARG, ERR_UNSUPPORTED (V > 8 388 608). */
 medusa_status rejection_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V, int K,
                                const float *logits, const float *head_logits, const int32_t *tree_tok,
                                float temperature, const float *u_node, const float *u_bonus,

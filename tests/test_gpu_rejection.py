@@ -152,3 +152,16 @@ def test_typical_eps_sweep_is_monotone_and_matches_oracle():
         if prev is not None:
             assert (ref["accept_len"] <= prev).all()
         prev = ref["accept_len"]
+
+
+def test_rejection_vocabulary_limit():
+    # past 8 Mi values the call refuses before any launch (small buffers stand
+    # in for the rows: nothing is read)
+    ot, t, K, k = make_tree("chain5")
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    ibuf = torch.zeros(64, dtype=torch.int32, device="cuda")
+    with pytest.raises(mb.MedusaError) as e:
+        mb.check(mb.lib.rejection_accept(mb._stream(), t.handle, 1, 8388609, K, mb._ptr(buf), mb._ptr(buf),
+                                         mb._ptr(ibuf), 1.0, mb._ptr(buf), mb._ptr(buf), mb._ptr(ibuf),
+                                         mb._ptr(ibuf), mb._ptr(ibuf), mb._ptr(ibuf), None))
+    assert e.value.status == mb.ERR_UNSUPPORTED
