@@ -325,7 +325,10 @@ medusa_status tree_attention_ragged(medusa_stream_t stream, medusa_dtype dt, con
  *  cand_p, row_thr [B][T]     device float, optional (NULL): p of each node's
  *                             token under its parent, and each row's threshold
  *                             (nan where not evaluated).
- *  Limits: eps, delta >= 0; temperature >= 0.  ws: typical_accept_workspace. */
+ *  Limits: eps, delta >= 0; temperature >= 0.  ws: typical_accept_workspace
+ *  bytes (the row pass's chunk partials, 32 bytes per sequence, node with
+ *  children and 4096-wide chunk of V, then 16 bytes per sequence for the
+ *  scan), 16-byte aligned. */
 size_t typical_accept_workspace(const medusa_tree *t, int B, int V);
 medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B, int V,
                              const float *logits, const int32_t *tree_tok, float eps,
@@ -340,7 +343,7 @@ medusa_status typical_accept(medusa_stream_t stream, const medusa_tree *t, int B
  * go to a 4 MiB array the library keeps in each GPU's memory for the life of
  * the process (looked up on the first call on a device); the call allocates
  * nothing.  Limit: B * (number of tree nodes with children) * ceil(V / 4096)
- * <= 131072, else MEDUSA_ERR_UNSUPPORTED with nothing enqueued.  All calls on
+ * + ceil(B / 2) <= 131072, else MEDUSA_ERR_UNSUPPORTED with nothing enqueued.  All calls on
  * one GPU share that array: calls that may overlap in time on one GPU (other
  * streams, other host threads) race and must be serialised by the caller. */
 medusa_status typical_accept_noalloc(medusa_stream_t stream, const medusa_tree *t, int B, int V,

@@ -15,6 +15,7 @@
 // next greedy token from its row.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -31,12 +32,28 @@ constexpr int kVec = 4;                        // float4 per thread: 4096-wide c
 constexpr int kScanThreads = 512;              // scan
 constexpr int kBatch = 8;                      // independent loads issued together
 constexpr int kLeafBatch = 16;                 // float4 loads per thread for a leaf row's argmax
+constexpr int kLeafParts = 8;                  // scan blocks per sequence (at most)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Part {  // 32 bytes
   float m, S, E, amax_val;
   int amax_idx, pad0, pad1, pad2;
 };
+
+// When the winner of sequence b is a leaf, the scan's blocks of b each take
+// the argmax of a share of its row and fold it into `key` (larger value
+// first, then smaller index); the last of them to count itself in `cnt`
+// decodes the token.  The row pass of the same call zeroes both.
+struct LeafSlot {  // 16 bytes
+  unsigned long long key;
+  unsigned int cnt, pad;
+};
+
+__device__ __forceinline__ unsigned long long argmax_order_key(float x, int i) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x == 0.f ? 0.f : x);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
+}
 
 // running statistics: max m of y, S = sum e^(y-m), E = sum e^(y-m)(y-m),
 // argmax (av, ai) of z with the lowest index on ties
@@ -110,9 +127,10 @@ __global__ __launch_bounds__(kThreads) void accept_rowpass(const float *__restri
                                                            int V, int n_internal,
                                                            const int32_t *__restrict__ internal,
                                                            int nchunks, float inv_tau, int greedy,
-                                                           Part *__restrict__ part) {
+                                                           Part *__restrict__ part, LeafSlot *__restrict__ leaf) {
   __shared__ Stat sh[kThreads / 64];
   const int chunk = blockIdx.x, slot = blockIdx.y, b = blockIdx.z;
+  if (leaf && chunk == 0 && slot == 0 && threadIdx.x == 0) leaf[b] = LeafSlot{0ull, 0u, 0u};
   const int row = internal[slot];
   const float *z = logits + ((size_t)b * T + row) * V;
   const int base = chunk * kThreads * VEC * 4;
@@ -189,13 +207,17 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
     const uint64_t *__restrict__ mask, float eps, float delta, float inv_tau, int greedy,
     const Part *__restrict__ part, int32_t *__restrict__ accept_len, int32_t *__restrict__ best_node,
     int32_t *__restrict__ next_tok, int32_t *__restrict__ accepted_tok, float *__restrict__ cand_p,
-    float *__restrict__ row_thr) {
+    float *__restrict__ row_thr, int nparts, LeafSlot *__restrict__ leaf) {
   __shared__ float s_m[MEDUSA_MAX_TREE], s_S[MEDUSA_MAX_TREE], s_thr[MEDUSA_MAX_TREE];
   __shared__ int s_amax[MEDUSA_MAX_TREE];
   __shared__ unsigned int s_dec[MEDUSA_MAX_TREE / 32];
   __shared__ unsigned int s_key[kScanThreads / 64];
   __shared__ Stat sh[kScanThreads / 64];
-  const int b = blockIdx.x;
+  // nparts blocks per sequence: each takes the same decisions (from the same
+  // inputs, so they agree on the winner); part 0 writes the outputs, and a
+  // leaf winner's row is shared out among all of them for its argmax
+  const int b = blockIdx.x / nparts, part_id = blockIdx.x % nparts;
+  const bool writer = part_id == 0;
   const int tid = threadIdx.x;
   for (int w = tid; w < MEDUSA_MAX_TREE / 32; w += kScanThreads) s_dec[w] = 0u;
 
@@ -262,9 +284,9 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
     const int c = tid + i * kScanThreads;
     if (c >= T) continue;
     const int sc = c_slot[i];
-    if (row_thr) row_thr[(size_t)b * T + c] = sc >= 0 ? s_thr[sc] : NAN;
+    if (row_thr && writer) row_thr[(size_t)b * T + c] = sc >= 0 ? s_thr[sc] : NAN;
     if (c == 0) {
-      if (cand_p) cand_p[(size_t)b * T] = NAN;
+      if (cand_p && writer) cand_p[(size_t)b * T] = NAN;
       continue;
     }
     const int sl = c_pslot[i];
@@ -283,7 +305,7 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
       p = exp2f((c_z[i] * inv_tau - s_m[sl]) * kLog2e) / s_S[sl];
       dec = p > s_thr[sl];
     }
-    if (cand_p) cand_p[(size_t)b * T + c] = p;
+    if (cand_p && writer) cand_p[(size_t)b * T + c] = p;
     if (dec) atomicOr(&s_dec[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
@@ -314,7 +336,7 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   const int alen = (int)(key >> 16);
   const int best = (int)(0xFFFFu - (key & 0xFFFFu));
 
-  if (tid == 0) {
+  if (tid == 0 && writer) {
     accept_len[b] = alen;
     best_node[b] = best;
     int32_t *at = accepted_tok + (size_t)b * (depth_max + 1);
@@ -325,32 +347,50 @@ __global__ __launch_bounds__(kScanThreads) void accept_scan(
   // 4. next greedy token: argmax of the winner's row (already known for rows with children)
   const int sb = slot_of[best];
   if (sb >= 0) {
-    if (tid == 0) next_tok[b] = s_amax[sb];
+    if (tid == 0 && writer) next_tok[b] = s_amax[sb];
     return;
   }
+  // the leaf's row, this block's share: float4 index range [q0, q1) (element
+  // range when V is not a multiple of 4)
   const float *z = logits + ((size_t)b * T + best) * V;
   Stat st = empty_stat();
   if ((V % 4) == 0) {
-    // a 32768-wide row in one round of loads (16 float4 per thread, issued
-    // unconditionally at clamped indices; indices past the row are skipped)
-    const int V4 = V / 4;
-    for (int base = tid; base < V4; base += kScanThreads * kLeafBatch) {
+    // up to a 32768-wide share in one round of loads (16 float4 per thread,
+    // issued unconditionally at clamped indices; indices past it are skipped)
+    const int V4 = V / 4, per = (V4 + nparts - 1) / nparts;
+    const int q0 = min(V4, part_id * per), q1 = min(V4, q0 + per);
+    for (int base = q0 + tid; base < q1; base += kScanThreads * kLeafBatch) {
       f32x4_t v[kLeafBatch];
 #pragma unroll
       for (int u = 0; u < kLeafBatch; ++u)
-        v[u] = *reinterpret_cast<const f32x4_t *>(z + 4 * min(base + u * kScanThreads, V4 - 1));
+        v[u] = *reinterpret_cast<const f32x4_t *>(z + 4 * min(base + u * kScanThreads, q1 - 1));
 #pragma unroll
       for (int u = 0; u < kLeafBatch; ++u)
-        if (base + u * kScanThreads < V4) {
+        if (base + u * kScanThreads < q1) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) arg_better(st.av, st.ai, v[u][j], 4 * (base + u * kScanThreads) + j);
         }
     }
   } else {
-    for (int i = tid; i < V; i += kScanThreads) arg_better(st.av, st.ai, z[i], i);
+    const int per = (V + nparts - 1) / nparts;
+    const int e0 = min(V, part_id * per), e1 = min(V, e0 + per);
+    for (int i = e0 + tid; i < e1; i += kScanThreads) arg_better(st.av, st.ai, z[i], i);
   }
   st = block_reduce<kScanThreads>(st, sh);
-  if (tid == 0) next_tok[b] = st.ai;
+  if (tid != 0) return;
+  if (nparts == 1) {
+    next_tok[b] = st.ai;
+    return;
+  }
+  // fold this share's argmax into the sequence's key; the count is an
+  // acquire-release step, so the last block to count sees every block's fold
+  __hip_atomic_fetch_max(&leaf[b].key, argmax_order_key(st.av, st.ai), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned int seen = __hip_atomic_fetch_add(&leaf[b].cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (seen == (unsigned int)nparts - 1u) {
+    const unsigned long long k = __hip_atomic_load(&leaf[b].key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    next_tok[b] = (int32_t)(~(uint32_t)k);
+  }
 }
 
 inline int chunks_for(int V) { return (V + kThreads * kVec * 4 - 1) / (kThreads * kVec * 4); }
@@ -392,9 +432,17 @@ medusa_status scratch_on_device(const char *who, Part **out) {
 
 }  // namespace
 
+// the row pass's chunk partials, then one LeafSlot per sequence
+inline size_t partials_for(const medusa_tree *t, int B, int V) {
+  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V);
+}
+inline size_t workspace_bytes(const medusa_tree *t, int B, int V) {
+  return partials_for(t, B, V) * sizeof(Part) + (size_t)B * sizeof(LeafSlot);
+}
+
 extern "C" size_t typical_accept_workspace(const medusa_tree *t, int B, int V) {
   if (!t || B < 1 || V < 1) return 0;
-  return (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V) * sizeof(Part);
+  return workspace_bytes(t, B, V);
 }
 
 namespace {
@@ -420,16 +468,22 @@ medusa_status typical_accept_impl(const char *who, medusa_stream_t stream, const
   const int nchunks = chunks_for(V);
   const int greedy = temperature == 0.f;
   const float inv_tau = greedy ? 1.f : 1.f / temperature;
+  // scan blocks per sequence: a leaf winner's row is read by all of them
+  // (one CU pulls a 128 KB row in about 5 us; eight shares take about 1 us);
+  // with no row pass (a root-only tree) nothing zeroes the leaf slots, and
+  // one block reads the row
+  const int nparts = t->n_internal > 0 ? std::max(1, std::min(kLeafParts, (V + 4095) / 4096)) : 1;
+  LeafSlot *leaf = nparts > 1 ? reinterpret_cast<LeafSlot *>(part + partials_for(t, B, V)) : nullptr;
   if (t->n_internal > 0) {
     MEDUSA_LAUNCH(who, (accept_rowpass<kVec>), dim3(nchunks, t->n_internal, B), dim3(kThreads), 0, st,
-                  logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part);
+                  logits, t->T, V, t->n_internal, t->d_internal, nchunks, inv_tau, greedy, part, leaf);
     medusa_status s = check_launch(who);
     if (s != MEDUSA_OK) return s;
   }
-  MEDUSA_LAUNCH(who, accept_scan, dim3(B), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
+  MEDUSA_LAUNCH(who, accept_scan, dim3(B * nparts), dim3(kScanThreads), 0, st, logits, tree_tok, t->T, t->W, V,
                 t->depth_max, t->n_internal, nchunks, t->d_slot, t->d_parent, t->d_depth, t->d_mask,
                 eps, delta, inv_tau, greedy, part, accept_len, best_node, next_tok, accepted_tok,
-                cand_p, row_thr);
+                cand_p, row_thr, nparts, leaf);
   return check_launch(who);
 }
 
@@ -479,16 +533,17 @@ extern "C" medusa_status typical_accept_noalloc(medusa_stream_t stream, const me
   medusa_status s = typical_accept_args(who, t, B, V, logits, tree_tok, eps, delta, temperature, accept_len,
                                         best_node, next_tok, accepted_tok);
   if (s != MEDUSA_OK) return s;
-  const size_t need = (size_t)B * (t->n_internal > 0 ? t->n_internal : 1) * chunks_for(V);
+  // partials, then the leaf slots (two to a Part)
+  const size_t need = partials_for(t, B, V) + ((size_t)B + 1) / 2;
   if (need > kScratchParts)
     return fail(MEDUSA_ERR_UNSUPPORTED,
-                "%s: B * internal nodes * ceil(V/4096) = %zu partials exceed the %zu of the library's scratch",
+                "%s: B * internal nodes * ceil(V/4096) + B/2 = %zu partials exceed the %zu of the library's scratch",
                 who, need, kScratchParts);
   Part *part = nullptr;
   s = scratch_on_device(who, &part);
   if (s != MEDUSA_OK) return s;
-  // every partial the scan reads is written by the row pass of the same call,
-  // so nothing needs clearing
+  // every partial and leaf slot the scan reads is written by the row pass of
+  // the same call, so nothing needs clearing
   return typical_accept_impl(who, stream, t, B, V, logits, tree_tok, eps, delta, temperature, accept_len,
                              best_node, next_tok, accepted_tok, cand_p, row_thr, part);
 }

@@ -207,7 +207,7 @@ def test_workspace_sizes():
     assert mb.medusa_topk_workspace(64, 32000, 10) == 0              # one slice per row
     assert mb.medusa_topk_workspace(4, 70000, 10) == 4 * 3 * 10 * 8   # three sorted lists per row
     t = mb.Tree(oracle.dense_paths(2, 2), 2, 2)
-    assert mb.typical_accept_workspace(t, 3, 1000) == 3 * 3 * 1 * 32   # 3 internal rows, 1 chunk
+    assert mb.typical_accept_workspace(t, 3, 1000) == 3 * 3 * 1 * 32 + 3 * 16   # 3 internal rows, 1 chunk; scan slots
 
 
 def test_injected_launch_failure_returns_err_hip_before_launch(monkeypatch):
