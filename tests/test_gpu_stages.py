@@ -553,6 +553,24 @@ def test_accept_eps_to_zero_accepts_all():
     assert (gpu["accept_len"] == ot["depth_max"]).all() and (gpu["best"] == deepest).all()
 
 
+@pytest.mark.parametrize("V", [4097, 20003, 32000])
+def test_accept_leaf_winner_row_split_between_blocks(V):
+    # eps -> 0 accepts every candidate, so the winner is the chain's leaf and
+    # the next token is its row's argmax, which the scan's blocks of a sequence
+    # share out; two equal maxima in different blocks' shares: the lower index wins
+    ot, t, tok, logits = accept_case(CHAIN5, 5, 1, 3, V, seed=V)
+    logits = np.clip(logits, -10, 10).astype(np.float32)
+    leaf = int(np.flatnonzero(ot["depth"] == ot["depth_max"])[0])
+    for b in range(3):
+        i1, i2 = 7 + 31 * b, V - 5 - 17 * b
+        logits[b, leaf, i1] = logits[b, leaf, i2] = 50.0
+    gpu = run_accept(t, logits, tok, 1e-30, 0.3, 1.0)
+    assert (gpu["best"] == leaf).all() and (gpu["accept_len"] == ot["depth_max"]).all()
+    want = [int(np.argmax(logits[b, leaf])) for b in range(3)]
+    assert want == [7 + 31 * b for b in range(3)]
+    assert gpu["next_tok"].tolist() == want
+
+
 def test_accept_uniform_rows():
     ot, t, tok, _ = accept_case(oracle.dense_paths(2, 2), 2, 2, 2, 640, seed=6)
     logits = np.zeros((2, ot["T"], 640), np.float32)
