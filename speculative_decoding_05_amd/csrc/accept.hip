@@ -397,12 +397,13 @@ inline int chunks_for(int V) { return (V + kThreads * kVec * 4 - 1) / (kThreads 
 
 }  // namespace
 
-// Scratch of typical_accept_noalloc: the row pass's chunk partials, in device
-// memory the library owns for the life of the process (one copy per GPU).
-// 131072 partials of 32 bytes = 4 MiB: B * internal nodes * ceil(V / 4096)
-// must not exceed that (the 341-node dense tree at batch 32 and V = 32000
-// needs 21760).  Host code never uses this name as an address: it looks the
-// device address up once per device (scratch_on_device below).
+// Scratch of typical_accept_noalloc: the row pass's chunk partials, then the
+// scan's leaf slots (two to a partial), in device memory the library owns for
+// the life of the process (one copy per GPU).  131072 partials of 32 bytes =
+// 4 MiB: B * internal nodes * ceil(V / 4096) + ceil(B / 2) must not exceed
+// that (the 341-node dense tree at batch 32 and V = 32000 needs 21776).  Host
+// code never uses this name as an address: it looks the device address up
+// once per device (scratch_on_device below).
 constexpr size_t kScratchParts = 131072;
 static __device__ __align__(256) Part scratch[kScratchParts];
 
