@@ -533,6 +533,7 @@ def run_accept(t, logits, tok, eps, delta, tau, ws=None):
     ("dense44", 2, 5000, 1.3), ("root", 3, 700, 1.0), ("chain5", 4, 4097, 1.0),
     ("dense44", 25, 20000, 1.0),                     # >= 2048 rows: wide row-pass chunks
     ("root", 2, 1, 1.0), ("chain5", 2, 1, 1.0),      # a vocabulary of one token: p = 1 everywhere
+    ("greedy64", 2, 70000, 1.0), ("chain5", 2, 131075, 0.0),   # vocabularies past 32768 (17 and 33 chunks)
 ])
 def test_accept_parity(tree, B, V, tau):
     say("accept", tree, B, V, tau)
