@@ -44,12 +44,17 @@ def elem(cfg):
 
 def stage_bytes(cfg, tree):
     """Algorithmic HBM bytes of each stage of one step (each tensor moved once)."""
+    from speculative_decoding_05_amd import step as st
     e, B, K, H, V = elem(cfg), cfg.B, cfg.K, cfg.H, cfg.V
     n_int = len(set(tree.parent[1:].tolist()))          # nodes with children
+    # with tile maxima the projection also writes one image per 16 logits and
+    # the top-k reads those images plus k candidate tiles of 64 bytes per row
+    tm = st.uses_tile_max(cfg)
+    images = K * B * ((V + 15) // 16) * 4
     return {
         "head_resblock": K * H * H * e + B * H * e + K * B * H * e,
-        "head_vocab": K * V * H * e + K * B * H * e + K * B * V * 4,
-        "topk_tokens": K * B * V * 4,
+        "head_vocab": K * V * H * e + K * B * H * e + K * B * V * 4 + (images if tm else 0),
+        "topk_tokens": images + K * B * cfg.k * 64 if tm else K * B * V * 4,
         "attention": 2 * B * cfg.nh * cfg.L * cfg.dh * e + 4 * B * tree.T * cfg.nh * cfg.dh * e,
         "accept": B * n_int * V * 4 + B * V * 4,
     }

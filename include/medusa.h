@@ -35,7 +35,7 @@
  *
  * Debug environment variables (read by the device calls; off by default):
  *  - MEDUSA_VALIDATE=1: before their kernels, medusa_topk and
- *    medusa_topk_tree_tokens check the logits for NaN and the root tokens
+ *    medusa_topk_tree_tokens[_tmax] check the logits for NaN and the root tokens
  *    for ids outside [0, V); typical_accept and rejection_accept check their
  *    logits for NaN and +inf and the tree tokens for ids outside [0, V).  A
  *    finding returns MEDUSA_ERR_NONFINITE (logits) or MEDUSA_ERR_ARG (ids)
@@ -151,6 +151,19 @@ medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K, int M, int
                                        const void *r, const void *W2p, float *logits);
 medusa_status medusa_heads_packed(medusa_stream_t stream, int K, int M, int H, int V, int group,
                                   const void *h, const void *W1p, const void *W2p, void *r, float *logits);
+
+/* medusa_head_vocab_packed that also writes, for medusa_topk_tree_tokens_tmax,
+ * the image of each 16-value tile's largest logit:
+ *   tile_max [K][M][ceil(V/16)] device uint32 (output, 4-byte aligned),
+ *   tile_max[k][m][t] = max of image(logits[k][m][v]) over v in
+ *   [16t, min(16t + 16, V)),
+ * where image(x) is the order-preserving map of the float's bits (-0.0 taken
+ * as +0.0; the sign bit set for x >= +0, every bit inverted for x < 0), so
+ * that images order as the values do.  The logits are bit-identical to
+ * medusa_head_vocab_packed's.  M <= MEDUSA_MAX_HEADS_M (ERR_UNSUPPORTED
+ * beyond); other errors as medusa_head_vocab_packed. */
+medusa_status medusa_head_vocab_packed_tmax(medusa_stream_t stream, int K, int M, int H, int V, int group,
+                                            const void *r, const void *W2p, float *logits, uint32_t *tile_max);
 
 /* Workspace variants of the packed calls, for many rows (the verify-pass
  * shape M = B*T, and the backbone's LM head over the tree nodes).  Same
@@ -270,6 +283,18 @@ medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, i
 medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B, int K, int V,
                                       int k, const float *logits, const int32_t *root_tok,
                                       int32_t *topk_idx, int32_t *tree_tok, void *ws, size_t ws_bytes);
+
+/* medusa_topk_tree_tokens from tile maxima: tile_max [K][B][ceil(V/16)] is
+ * what medusa_head_vocab_packed_tmax wrote together with these logits (with
+ * any other contents the result is unspecified).  A row's top k lie in the
+ * tiles whose image reaches a bound taken from the tile images, so each row
+ * reads its tile images and then only those tiles instead of all V logits.
+ * Outputs are identical to medusa_topk_tree_tokens'.  No workspace.  Errors
+ * as medusa_topk_tree_tokens, plus ERR_UNSUPPORTED for V > 524288 or
+ * K*B > 65535 and ERR_ARG for a NULL or misaligned tile_max. */
+medusa_status medusa_topk_tree_tokens_tmax(medusa_stream_t stream, const medusa_tree *t, int B, int K, int V,
+                                           int k, const float *logits, const uint32_t *tile_max,
+                                           const int32_t *root_tok, int32_t *topk_idx, int32_t *tree_tok);
 
 /* ------------------------------------------------------------------------- */
 /* (3) Tree attention.  Paper summary, "基准/方法设计" (second component) and the

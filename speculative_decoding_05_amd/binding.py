@@ -44,6 +44,7 @@ SIGNATURES = {
     "medusa_pack_weights": (_i, [_p, _i, _i, _i, _i, _p, _p]),
     "medusa_head_resblock_packed": (_i, [_p, _i, _i, _i, _i, _p, _p, _p]),
     "medusa_head_vocab_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p]),
+    "medusa_head_vocab_packed_tmax": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p]),
     "medusa_heads_packed": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
     "medusa_head_workspace": (_sz, [_i, _i, _i]),
     "medusa_head_resblock_packed_ws": (_i, [_p, _i, _i, _i, _i, _p, _p, _p, _p, _sz]),
@@ -62,6 +63,7 @@ SIGNATURES = {
     "medusa_tree_free": (None, [_p]),
     "medusa_tree_tokens": (_i, [_p, _p, _i, _i, _i, _p, _p, _p]),
     "medusa_topk_tree_tokens": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz]),
+    "medusa_topk_tree_tokens_tmax": (_i, [_p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _p]),
     "tree_attention_workspace": (_sz, [_i, _p, _i, _i, _i, _i]),
     "tree_attention": (_i, [_p, _i, _p, _i, _i, _i, _i, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
     "tree_attention_ragged": (_i, [_p, _i, _p, _i, _i, _i, _i, _i, _p, _f, _p, _p, _p, _p, _p, _p, _p, _sz]),
@@ -188,6 +190,14 @@ def medusa_head_vocab_packed(r, W2p, logits):
     _dev(r, logits)
     check(lib.medusa_head_vocab_packed(_stream(), W2p.K, r.shape[1], W2p.H, W2p.N, W2p.group, _ptr(r),
                                        _ptr(W2p.data), _ptr(logits)))
+    return logits
+
+
+def medusa_head_vocab_packed_tmax(r, W2p, logits, tile_max):
+    """As medusa_head_vocab_packed, also writing tile_max [K][M][ceil(V/16)] (int32 tensor of uint32 images)."""
+    _dev(r, logits, tile_max)
+    check(lib.medusa_head_vocab_packed_tmax(_stream(), W2p.K, r.shape[1], W2p.H, W2p.N, W2p.group, _ptr(r),
+                                            _ptr(W2p.data), _ptr(logits), _ptr(tile_max)))
     return logits
 
 
@@ -351,6 +361,15 @@ def medusa_topk_tree_tokens(tree, logits, k, root_tok, topk_idx, tree_tok, ws=No
         ws = workspace(medusa_topk_workspace(K * B, V, k), logits.device)
     check(lib.medusa_topk_tree_tokens(_stream(), tree.handle, B, K, V, k, _ptr(logits), _ptr(root_tok),
                                       _ptr(topk_idx), _ptr(tree_tok), _ptr(ws), ws.numel()))
+    return tree_tok
+
+
+def medusa_topk_tree_tokens_tmax(tree, logits, tile_max, k, root_tok, topk_idx, tree_tok):
+    """medusa_topk_tree_tokens reading the tile maxima written with the logits."""
+    _dev(logits, tile_max, root_tok, topk_idx, tree_tok)
+    K, B, V = logits.shape
+    check(lib.medusa_topk_tree_tokens_tmax(_stream(), tree.handle, B, K, V, k, _ptr(logits), _ptr(tile_max),
+                                           _ptr(root_tok), _ptr(topk_idx), _ptr(tree_tok)))
     return tree_tok
 
 

@@ -107,6 +107,30 @@ __device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
   o = dpp64<kDppMirror>(v); v = o > v ? o : v;
   return v;
 }
+// Buffer resource word 3 on gfx9 for raw 32-bit loads.  A raw buffer load
+// whose byte offset (in the vector register) is at or past the resource's size
+// returns 0 without touching memory, so bounds checks need no branch.
+constexpr int kBufferWord3 = 0x00020000;
+
+// max over the 16 lanes of each row (result in every lane of the row)
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  uint32_t o;
+  o = dpp<kDppXor1>(v); v = o > v ? o : v;
+  o = dpp<kDppXor2>(v); v = o > v ? o : v;
+  o = dpp<kDppHalfMirror>(v); v = o > v ? o : v;
+  o = dpp<kDppMirror>(v); v = o > v ? o : v;
+  return v;
+}
+
+// Order-preserving 32-bit image of a float, -0.0 folded onto +0.0: for
+// non-NaN a, b, a > b exactly when image(a) > image(b).  Positive NaNs map
+// above +inf, negative NaNs below -inf (the all-ones pattern to 0).
+__device__ __forceinline__ uint32_t order_image(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   uint32_t o;
   o = dpp<kDppXor1>(v); v = o > v ? o : v;

@@ -44,7 +44,7 @@ template <int R, int C, int EPI, bool PACKED, int U, int NW>
 __global__ __launch_bounds__(64 * NW) void head_gemm_bf16(
     const uint16_t *__restrict__ W, const uint16_t *__restrict__ X, long x_head_stride, int N,
     int H, int M_total, int m0, int Mg, int tiles_per_head, int lgG, const uint16_t *__restrict__ resid,
-    uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32) {
+    uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32, uint32_t *__restrict__ tile_img) {
   __shared__ float red[NW][16 * C][16 * R + 1];
   const int head = blockIdx.x / tiles_per_head;
   const int n0 = (blockIdx.x % tiles_per_head) * 16 * R;
@@ -137,17 +137,29 @@ __global__ __launch_bounds__(64 * NW) void head_gemm_bf16(
       for (int v = 0; v < 4; ++v) red[wave][c * 16 + lr][r * 16 + lg * 4 + v] = acc[r][c][v];
   __syncthreads();
 
+  // The lanes active in an iteration are whole waves (16*C*16*R is a multiple
+  // of 256, the stride of 64), and the 16 lanes of a row hold the 16 columns
+  // of one weight tile for one activation row: the optional tile maxima are
+  // one row reduction.
   for (int e = threadIdx.x; e < 16 * C * 16 * R; e += 64 * NW) {
     const int m = e / (16 * R), nl = e % (16 * R);
     const int n = n0 + nl;
-    if (m >= Mg || n >= N) continue;
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][m][nl];
+    const bool ok = m < Mg && n < N;
     const size_t o = ((size_t)head * M_total + m0 + m) * N + n;
     if (EPI == EPI_LOGITS) {
-      out_f32[o] = v;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][m][nl];
+      if (ok) out_f32[o] = v;
+      if (tile_img) {
+        const uint32_t t = row_max_u32(ok ? order_image(v) : 0u);
+        if (ok && (nl & 15) == 0) tile_img[((size_t)head * M_total + m0 + m) * ((N + 15) / 16) + n / 16] = t;
+      }
     } else {
+      if (!ok) continue;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][m][nl];
       const float hv = bf16_to_f32(resid[(size_t)(m0 + m) * H + n]);
       out_bf16[o] = f32_to_bf16_rne(hv + v / (1.0f + expf(-v)));
     }
@@ -233,10 +245,10 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t *__res
 
 template <int R, int C, int EPI, bool PACKED, int U, int NW>
 medusa_status launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K, int N, int H, int M,
-                int m0, int Mg, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+                int m0, int Mg, int lgG, const uint16_t *resid, uint16_t *ob, float *of, uint32_t *timg) {
   const int tiles = (N + 16 * R - 1) / (16 * R);
   MEDUSA_LAUNCH("medusa heads", (head_gemm_bf16<R, C, EPI, PACKED, U, NW>), dim3(tiles * K), dim3(64 * NW), 0, st, W, X, xhs,
-                     N, H, M, m0, Mg, tiles, lgG, resid, ob, of);
+                     N, H, M, m0, Mg, tiles, lgG, resid, ob, of, timg);
   return MEDUSA_OK;
 }
 
@@ -252,30 +264,31 @@ medusa_status launch_one(hipStream_t st, const uint16_t *W, const uint16_t *X, l
 // 22.3 us, at 5 rows it would be slower).
 template <int EPI, bool PACKED>
 medusa_status launch_bf16(hipStream_t st, const uint16_t *W, const uint16_t *X, long xhs, int K,
-                          int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of) {
+                          int N, int H, int M, int lgG, const uint16_t *resid, uint16_t *ob, float *of,
+                          uint32_t *timg = nullptr) {
   if (M >= kManyRows) return head_gemm_many_rows<EPI, PACKED>(st, W, X, xhs, K, N, H, M, lgG, resid, ob, of);
   const int m0 = 0, Mg = M;   // one group: the weights are streamed once
   medusa_status s;
   if (EPI == EPI_RESBLOCK && Mg <= 4 && H % (32 * 16) == 0)
-    s = launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 4, 16>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (EPI == EPI_RESBLOCK && Mg <= 8 && H % (32 * 8) == 0)
-    s = launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 4, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (EPI == EPI_RESBLOCK && Mg <= 16 && H % (32 * 8) == 0)
-    s = launch_one<4, 1, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<4, 1, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (Mg <= 4 && (H / kWaves / 32) % 16 == 0)
-    s = launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 16, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (Mg <= 4)
-    s = launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<1, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (EPI == EPI_LOGITS && Mg > 8 && Mg <= 16)
-    s = launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<8, 1, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (EPI == EPI_LOGITS && Mg > 16)
-    s = launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<8, 2, EPI, PACKED, 2, 2>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (Mg <= 16)
-    s = launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<2, 1, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else if (H % (32 * 8) == 0)
-    s = launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<4, 2, EPI, PACKED, 2, 8>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   else
-    s = launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of);
+    s = launch_one<2, 2, EPI, PACKED, 8, 4>(st, W, X, xhs, K, N, H, M, m0, Mg, lgG, resid, ob, of, timg);
   if (s != MEDUSA_OK) return s;
   return check_launch(EPI == EPI_LOGITS ? "medusa_head_vocab" : "medusa_head_resblock");
 }
@@ -416,6 +429,25 @@ extern "C" medusa_status medusa_head_vocab_packed(medusa_stream_t stream, int K,
   return launch_bf16<EPI_LOGITS, true>(as_stream(stream), static_cast<const uint16_t *>(W2p),
                                        static_cast<const uint16_t *>(r), (long)M * H, K, V, H, M, lgG, nullptr,
                                        nullptr, logits);
+}
+
+extern "C" medusa_status medusa_head_vocab_packed_tmax(medusa_stream_t stream, int K, int M, int H, int V,
+                                                       int group, const void *r, const void *W2p, float *logits,
+                                                       uint32_t *tile_max) {
+  TraceRange tr("medusa_head_vocab_packed_tmax");
+  medusa_status s = check_common("medusa_head_vocab_packed_tmax", MEDUSA_BF16, K, M, H);
+  if (s != MEDUSA_OK) return s;
+  const int lgG = group_log2(group);
+  if (lgG < 0) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed_tmax: group=%d not in {1, 2, 4, 8}", group);
+  if (V < 1) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed_tmax: V=%d", V);
+  if (M > MEDUSA_MAX_HEADS_M)
+    return fail(MEDUSA_ERR_UNSUPPORTED, "medusa_head_vocab_packed_tmax: M=%d > %d", M, MEDUSA_MAX_HEADS_M);
+  if (!r || !W2p || !logits || !tile_max) return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed_tmax: NULL pointer");
+  if (!aligned16(r) || !aligned16(W2p) || !aligned16(logits) || (reinterpret_cast<uintptr_t>(tile_max) & 3u))
+    return fail(MEDUSA_ERR_ARG, "medusa_head_vocab_packed_tmax: misaligned pointer");
+  return launch_bf16<EPI_LOGITS, true>(as_stream(stream), static_cast<const uint16_t *>(W2p),
+                                       static_cast<const uint16_t *>(r), (long)M * H, K, V, H, M, lgG, nullptr,
+                                       nullptr, logits, tile_max);
 }
 
 // Workspace variants: from kFragmentRows rows the activations are first

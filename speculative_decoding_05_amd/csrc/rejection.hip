@@ -27,7 +27,6 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxResid = MEDUSA_MAX_TREE;   // rejections at one node <= its children
-constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3 on gfx9: 32-bit elements
 
 __device__ __forceinline__ float wave_sum(float v) {
   v += dppf<kDppXor1>(v);

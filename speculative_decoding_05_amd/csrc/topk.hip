@@ -27,11 +27,6 @@ constexpr int kCandMax = 1024;   // candidates a slice can rank
 constexpr int kMergeMax = 4096;  // slices * k the merge can hold
 constexpr int kMergeThreads = 256;
 
-__device__ __forceinline__ uint32_t value_image(float v) {
-  uint32_t u = __builtin_bit_cast(uint32_t, v);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 __device__ __forceinline__ uint64_t make_key(uint32_t image, uint32_t idx) {
   return (static_cast<uint64_t>(image) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - idx);
 }
@@ -117,14 +112,14 @@ __global__ __launch_bounds__(NT) void topk_slices(const float *__restrict__ logi
     for (int g = 0; g < PT / 4; ++g) {
       const int i0 = min(index_of(4 * g), V - 4);
       const float4 f = *reinterpret_cast<const float4 *>(z + i0);
-      img[4 * g] = value_image(f.x);
-      img[4 * g + 1] = value_image(f.y);
-      img[4 * g + 2] = value_image(f.z);
-      img[4 * g + 3] = value_image(f.w);
+      img[4 * g] = order_image(f.x);
+      img[4 * g + 1] = order_image(f.y);
+      img[4 * g + 2] = order_image(f.z);
+      img[4 * g + 3] = order_image(f.w);
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < PT; ++e) img[e] = value_image(z[min(index_of(e), V - 1)]);
+    for (int e = 0; e < PT; ++e) img[e] = order_image(z[min(index_of(e), V - 1)]);
   }
   // images of indices >= V become 0, at or below every valid image
   uint32_t m = 0u;
@@ -180,7 +175,7 @@ __global__ __launch_bounds__(NT) void topk_slices(const float *__restrict__ logi
       for (int e = 0; e < PT; ++e) {
         const int i = index_of(e);
         const uint64_t key =
-            ((taken >> e) & 1u) || i >= V ? 0ull : make_key(value_image(z[i]), static_cast<uint32_t>(i));
+            ((taken >> e) & 1u) || i >= V ? 0ull : make_key(order_image(z[i]), static_cast<uint32_t>(i));
         if (key > best) {
           best = key;
           bi = e;
@@ -234,6 +229,130 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge(const float *__restr
   }
   __syncthreads();
   emit_row(logits + (size_t)row * V, row, k, s_out, idx, val, ts);
+}
+
+// Top-k from tile maxima.  With the logits come the images of each 16-value
+// tile's largest element (written by the vocabulary projection's blocks, which
+// hold a tile's 16 values together).  A row's tile images are dealt to the
+// threads in order, and the 64 sets {lane l of every wave} each take their
+// largest: theta, the largest set maximum that at least k set maxima reach, is
+// reached by k distinct tiles and so by k distinct elements, hence is at most
+// the row's k-th largest value.  The row's top k therefore lie in the tiles
+// whose image reaches theta: the block loads those tiles' values only (a
+// 32000-value row: 8 KB of images and typically a dozen 64-byte tiles, not
+// 128 KB) and ranks the candidate keys exactly as above.  Should the tiles or
+// the candidates overflow LDS (massive ties), k rounds each take the largest
+// key below the previous round's over the whole row.
+constexpr int kTileCand = 256;  // candidate tiles a row can load
+
+template <int PT>
+__global__ __launch_bounds__(1024) void topk_tiles(const float *__restrict__ logits,
+                                                   const uint32_t *__restrict__ timg, int V, int k,
+                                                   int32_t *__restrict__ idx, TokenScatter ts) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t s_lmax[NT / 64][64];
+  __shared__ int s_tile[kTileCand];
+  __shared__ uint64_t s_cand[kCandMax];
+  __shared__ uint64_t s_out[MEDUSA_MAX_TOPK];
+  __shared__ uint64_t s_wave[2][NT / 64];
+  __shared__ uint32_t s_theta;
+  __shared__ int s_ntile, s_cnt;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x;
+  const int nt = (V + 15) >> 4;
+  const float *z = logits + (size_t)row * V;
+  // tile e*NT + tid; reads past the row's nt images return 0, at or below
+  // every valid image
+  const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t *>(timg + (size_t)row * nt), (short)0, nt * 4, kBufferWord3);
+  uint32_t img[PT];
+#pragma unroll
+  for (int e = 0; e < PT; ++e) img[e] = __builtin_amdgcn_raw_buffer_load_b32(tr, (e * NT + tid) * 4, 0, 0);
+  uint32_t m = 0u;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) m = img[e] > m ? img[e] : m;
+  s_lmax[wave][lane] = m;
+  if (tid < MEDUSA_MAX_TOPK) s_out[tid] = 0ull;
+  if (tid == 0) {
+    s_ntile = 0;
+    s_cnt = 0;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t g = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) g = s_lmax[w][lane] > g ? s_lmax[w][lane] : g;
+    int reach = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) reach += readlane(g, j) >= g ? 1 : 0;
+    const uint32_t t = wave_max_u32(reach >= k ? g : 0u);
+    if (lane == 0) s_theta = t;
+  }
+  __syncthreads();
+  const uint32_t theta = s_theta;
+#pragma unroll
+  for (int e = 0; e < PT; ++e) {
+    const int t = e * NT + tid;
+    if (t < nt && img[e] >= theta) {
+      const int p = atomicAdd(&s_ntile, 1);
+      if (p < kTileCand) s_tile[p] = t;
+    }
+  }
+  __syncthreads();
+  const int ntile = s_ntile;
+  const bool tiles_fit = ntile <= kTileCand;
+  if (tiles_fit) {
+    // 64 tiles per pass, 16 lanes per tile; reads past the row return 0
+    const __amdgpu_buffer_rsrc_t zr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(z), (short)0, V * 4, kBufferWord3);
+    for (int s0 = 0; s0 < ntile; s0 += NT / 16) {
+      const int slot = s0 + (tid >> 4);
+      const bool in_list = slot < ntile;
+      const int i = s_tile[in_list ? slot : 0] * 16 + (tid & 15);
+      const bool valid = in_list && i < V;
+      const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(zr, (valid ? i : V) * 4, 0, 0));
+      const uint32_t im = order_image(x);
+      if (valid && im >= theta) {
+        const int p = atomicAdd(&s_cnt, 1);
+        if (p < kCandMax) s_cand[p] = make_key(im, static_cast<uint32_t>(i));
+      }
+    }
+  }
+  __syncthreads();
+  const int C = s_cnt;
+  if (tiles_fit && C <= kCandMax) {
+    for (int i = tid; i < C; i += NT) {
+      const uint64_t key = s_cand[i];
+      int rank = 0;
+      for (int j = 0; j < C; ++j) rank += s_cand[j] > key ? 1 : 0;
+      if (rank < k) s_out[rank] = key;
+    }
+  } else {
+    // keys are distinct, so "largest below the previous" needs no marks
+    uint64_t prev = ~0ull;
+    for (int round = 0; round < k; ++round) {
+      uint64_t best = 0ull;
+      for (int i = tid; i < V; i += NT) {
+        const uint64_t key = make_key(order_image(z[i]), static_cast<uint32_t>(i));
+        if (key < prev && key > best) best = key;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = shfl_xor_u64(best, off);
+        best = o > best ? o : best;
+      }
+      uint64_t *buf = s_wave[round & 1];  // alternate buffers: one barrier per round
+      if (lane == 0) buf[wave] = best;
+      __syncthreads();
+      uint64_t g = buf[0];
+#pragma unroll
+      for (int w = 1; w < NT / 64; ++w) g = buf[w] > g ? buf[w] : g;
+      prev = g;
+      if (tid == 0) s_out[round] = g;
+    }
+  }
+  __syncthreads();
+  emit_row(z, row, k, s_out, idx, nullptr, ts);
 }
 
 __global__ void tree_tokens_kernel(int B, int T, int k, const int32_t *__restrict__ depth,
@@ -319,6 +438,47 @@ extern "C" medusa_status medusa_topk_tree_tokens(medusa_stream_t stream, const m
   const TokenScatter ts = {tree_tok, t->d_rank, t->d_dstart, root_tok, B, t->T, t->depth_max};
   return topk_launch("medusa_topk_tree_tokens", as_stream(stream), K * B, V, k, logits, topk_idx, nullptr, ws,
                      ws_bytes, ts, B);
+}
+
+extern "C" medusa_status medusa_topk_tree_tokens_tmax(medusa_stream_t stream, const medusa_tree *t, int B,
+                                                      int K, int V, int k, const float *logits,
+                                                      const uint32_t *tile_max, const int32_t *root_tok,
+                                                      int32_t *topk_idx, int32_t *tree_tok) {
+  const char *who = "medusa_topk_tree_tokens_tmax";
+  TraceRange tr(who);
+  medusa_status s = check_tree_on_device(t);
+  if (s != MEDUSA_OK) return s;
+  if (B < 1 || K < 1 || V < 1) return fail(MEDUSA_ERR_ARG, "%s: B=%d K=%d V=%d", who, B, K, V);
+  if (!logits || !tile_max || !root_tok || !topk_idx || !tree_tok) return fail(MEDUSA_ERR_ARG, "%s: NULL pointer", who);
+  if (reinterpret_cast<uintptr_t>(tile_max) & 3u) return fail(MEDUSA_ERR_ARG, "%s: tile_max must be 4-byte aligned", who);
+  if (K < t->depth_max || k < t->k)
+    return fail(MEDUSA_ERR_SHAPE, "%s: top-k block [K=%d][k=%d] smaller than the tree's [%d][%d]", who, K, k,
+                t->depth_max, t->k);
+  if (k < 1 || k > V) return fail(MEDUSA_ERR_ARG, "%s: k=%d outside [1, V=%d]", who, k, V);
+  if (k > MEDUSA_MAX_TOPK) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: k=%d > %d", who, k, MEDUSA_MAX_TOPK);
+  const long R = (long)K * B;
+  if (R > 65535) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: K*B=%ld > 65535", who, R);
+  const int nt = (V + 15) / 16;
+  if (nt > kNT * 32) return fail(MEDUSA_ERR_UNSUPPORTED, "%s: V=%d > %d", who, V, kNT * 32 * 16);
+  const hipStream_t st = as_stream(stream);
+  if (validate_enabled()) {  // NaN logits; root tokens outside [0, V)
+    ValidateSpec v;
+    v.a = logits;
+    v.na = (size_t)R * V;
+    v.tok = root_tok;
+    v.nt = (size_t)B;
+    v.V = V;
+    medusa_status vs = validate_inputs(st, who, v);
+    if (vs != MEDUSA_OK) return vs;
+  }
+  const TokenScatter ts = {tree_tok, t->d_rank, t->d_dstart, root_tok, B, t->T, t->depth_max};
+  if (nt <= kNT * 2)
+    MEDUSA_LAUNCH("medusa_topk", topk_tiles<2>, dim3((unsigned)R), dim3(kNT), 0, st, logits, tile_max, V, k, topk_idx, ts);
+  else if (nt <= kNT * 8)
+    MEDUSA_LAUNCH("medusa_topk", topk_tiles<8>, dim3((unsigned)R), dim3(kNT), 0, st, logits, tile_max, V, k, topk_idx, ts);
+  else
+    MEDUSA_LAUNCH("medusa_topk", topk_tiles<32>, dim3((unsigned)R), dim3(kNT), 0, st, logits, tile_max, V, k, topk_idx, ts);
+  return check_launch(who);
 }
 
 extern "C" medusa_status medusa_tree_tokens(medusa_stream_t stream, const medusa_tree *t, int B,
