@@ -42,10 +42,10 @@ def uses_tile_max(cfg: configs.Config) -> bool:
     tiles per row instead of the whole row (about 6.9 -> 4.7 us per call).
     Measured per step on MI355X: 1.7 us faster at one row; at 8 and 32 rows
     the scattered image writes cost the projection 3.6-5.4 us, more than the
-    top-k saves, and at 16 rows the two are within noise.  Two rows write as
-    many images per call as 16 rows do (one per row and 16 logits there, one
-    per row and 128 logits at 16 rows), so they are taken as break-even or
-    better; two rows were not measured.
+    top-k saves, and at 16 rows the two are within noise.  Two rows cause as
+    many separate image writes per call as 16 rows do (there one block's
+    eight adjacent images of a row go out together), so they are taken as
+    break-even or better; two rows were not measured.
     """
     return cfg.dtype == "bf16" and cfg.B <= 2
 
